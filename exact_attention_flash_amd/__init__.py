@@ -1,1 +1,86 @@
-"""MI355X-native exact attention forward (FlashAttention-style), bf16/fp16."""
+"""MI355X-native exact attention forward (FlashAttention-style), bf16/fp16.
+
+The computation runs entirely in the gfx950 HIP kernels behind the C ABI of
+include/flash_attn.h; this module only checks and marshals torch tensors
+(device memory and streams) into that call. If the library is missing the call
+raises: there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import math
+
+from . import _native
+from ._native import (FA_BF16, FA_FP16, FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEADDIM,  # noqa: F401
+                      FA_ERR_DTYPE, FA_ERR_SCALE, FA_ERR_ALIGN, FA_ERR_ALIAS, FA_ERR_HIP, FA_ERR_ARG)
+
+__all__ = ["forward", "flash_attn_fwd", "flash_attn_strerror", "flash_attn_abi_version"]
+
+
+class FlashAttnError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(f"flash_attn_fwd failed ({status}): {_native.strerror(status)}")
+
+
+def _dtype_code(t):
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    if t.dtype == torch.float16:
+        return FA_FP16
+    raise TypeError(f"q/k/v must be bfloat16 or float16, got {t.dtype}")
+
+
+def flash_attn_fwd(q, k, v, o, lse, causal: bool = False, scale: float | None = None, stream=None) -> None:
+    """Run the kernel on caller-owned tensors (the C entry point with torch arguments).
+
+    q, k, v, o: contiguous [B, H, N, d] bf16/fp16 CUDA tensors of one dtype;
+    lse: contiguous [B, H, N] float32. ``stream`` is a torch.cuda.Stream (default:
+    the current stream). Asynchronous, like the C call.
+    """
+    import torch
+
+    if q.dim() != 4:
+        raise ValueError("q must have shape [B, H, N, d]")
+    for name, t in (("k", k), ("v", v), ("o", o)):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{name} must match q in shape and dtype")
+    B, H, N, d = q.shape
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 with shape [B, H, N]")
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.device != q.device:
+            raise ValueError("all tensors must be on one device")
+    dtype = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = _native.fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                         B, H, N, d, causal, scale, stream.cuda_stream, dtype)
+    if st != FA_OK:
+        raise FlashAttnError(st)
+
+
+def forward(q, k, v, causal: bool = False, scale: float | None = None, stream=None):
+    """Allocate O (q's dtype) and LSE (float32) and run the forward pass. Returns (o, lse)."""
+    import torch
+
+    B, H, N, _ = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    flash_attn_fwd(q, k, v, o, lse, causal=causal, scale=scale, stream=stream)
+    return o, lse
+
+
+def flash_attn_strerror(status: int) -> str:
+    return _native.strerror(status)
+
+
+def flash_attn_abi_version() -> int:
+    return _native.abi_version()

@@ -1,0 +1,66 @@
+"""ctypes view of the C ABI declared in include/flash_attn.h."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from .build import LIB_PATH
+
+FA_BF16 = 0
+FA_FP16 = 1
+
+FA_OK = 0
+FA_ERR_NULL = -1
+FA_ERR_SHAPE = -2
+FA_ERR_HEADDIM = -3
+FA_ERR_DTYPE = -4
+FA_ERR_SCALE = -5
+FA_ERR_ALIGN = -6
+FA_ERR_ALIAS = -7
+FA_ERR_HIP = -8
+FA_ERR_ARG = -9
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the built library once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"HIP library {LIB_PATH} is missing: build it with exact_attention_flash_amd.build.build() "
+                "(or __graft_entry__.build()); there is no fallback path")
+        L = ctypes.CDLL(LIB_PATH)
+        L.flash_attn_fwd.restype = ctypes.c_int
+        L.flash_attn_fwd.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_int,
+        ]
+        L.flash_attn_fwd_validate.restype = ctypes.c_int
+        L.flash_attn_fwd_validate.argtypes = L.flash_attn_fwd.argtypes
+        L.flash_attn_strerror.restype = ctypes.c_char_p
+        L.flash_attn_strerror.argtypes = [ctypes.c_int]
+        L.flash_attn_abi_version.restype = ctypes.c_int
+        L.flash_attn_abi_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+def fwd_raw(q, k, v, o, lse, B, H, N, d, causal, scale, stream, dtype) -> int:
+    """Call flash_attn_fwd with integer addresses; returns the status code."""
+    return lib().flash_attn_fwd(q, k, v, o, lse, B, H, N, d, int(causal), float(scale), stream, dtype)
+
+
+def validate_raw(q, k, v, o, lse, B, H, N, d, causal, scale, stream, dtype) -> int:
+    """Call flash_attn_fwd_validate (host checks only, never launches)."""
+    return lib().flash_attn_fwd_validate(q, k, v, o, lse, B, H, N, d, int(causal), float(scale), stream, dtype)
+
+
+def strerror(status: int) -> str:
+    return lib().flash_attn_strerror(int(status)).decode()
+
+
+def abi_version() -> int:
+    return lib().flash_attn_abi_version()

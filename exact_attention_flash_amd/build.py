@@ -1,0 +1,65 @@
+"""Compile the HIP library in-tree for gfx950 with hipcc.
+
+The shared library ``libflash_attn_mi355x.so`` is written next to this file so
+that it travels with the source tree; nothing is installed elsewhere.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+REPO_DIR = os.path.dirname(PKG_DIR)
+LIB_NAME = "libflash_attn_mi355x.so"
+LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+SOURCES = [
+    os.path.join(PKG_DIR, "csrc", "fwd_kernel.hip"),
+    os.path.join(PKG_DIR, "csrc", "flash_attn.cpp"),
+]
+# Packed fp32 VALU instructions are disabled for device code: the compiler
+# otherwise forms them from plain float code.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+ARCH = "gfx950"
+
+
+def hipcc_path() -> str:
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cand = os.path.join(rocm, "bin", "hipcc")
+    if os.path.exists(cand):
+        return cand
+    found = shutil.which("hipcc")
+    if not found:
+        raise RuntimeError("hipcc not found (set ROCM_PATH)")
+    return found
+
+
+def command(out_path: str, extra=()) -> list:
+    return [hipcc_path(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
+            "-Wall", *DEVICE_FLAGS, f"-I{os.path.join(REPO_DIR, 'include')}", *extra,
+            "-o", out_path, *SOURCES]
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    """Compile every source into LIB_PATH (always recompiles). Returns the path."""
+    tmp = LIB_PATH + f".tmp{os.getpid()}"
+    cmd = command(tmp, extra)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    # the host pass warns that it does not know the device-only feature flag
+    noise = "unknown target feature"
+    msgs = [ln for ln in res.stdout.splitlines() if noise not in ln and "packed-fp32-ops" not in ln]
+    if res.returncode != 0:
+        if os.path.exists(tmp):
+            os.remove(tmp)
+        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    if verbose and msgs:
+        print("\n".join(msgs), file=sys.stderr)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

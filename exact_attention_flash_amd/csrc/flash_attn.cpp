@@ -1,0 +1,112 @@
+// C ABI of the attention forward: host-side validation and dispatch.
+// Every check runs before anything touches the GPU, so the error paths can be
+// exercised on a machine without one.
+#include "flash_attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "fwd_kernel.h"
+
+namespace {
+
+bool overlaps(const void* a, uint64_t an, const void* b, uint64_t bn) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + bn && y < x + an;
+}
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+}  // namespace
+
+extern "C" int flash_attn_abi_version(void) { return 1; }
+
+extern "C" const char* flash_attn_strerror(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "B, H or N is negative or too large for the kernel's indexing";
+    case FA_ERR_HEADDIM: return "head dimension d must be 64 or 128";
+    case FA_ERR_DTYPE: return "dtype must be FA_BF16 or FA_FP16";
+    case FA_ERR_SCALE: return "scale must be finite and > 0";
+    case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
+    case FA_ERR_ALIAS: return "o or lse overlaps an input, or o overlaps lse";
+    case FA_ERR_HIP: return "HIP runtime error at launch";
+    case FA_ERR_ARG: return "causal must be 0 or 1";
+    default: return "unknown status";
+  }
+}
+
+namespace {
+
+// All host-side checks; on success fills the launch arguments.
+int check_args(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+               int64_t N, int64_t d, int causal, float scale, int dtype, fa::FwdArgs* a, bool* empty) {
+  *empty = false;
+  if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (dtype != FA_BF16 && dtype != FA_FP16) return FA_ERR_DTYPE;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
+  if (B == 0 || H == 0 || N == 0) {
+    *empty = true;
+    return FA_OK;
+  }
+
+  // indexing limits: a (batch, head) slice is addressed with 32-bit offsets,
+  // workgroups with a 32-bit grid
+  const int64_t rows = fa::rows_per_workgroup();
+  if (N * d > INT32_MAX - 1) return FA_ERR_SHAPE;
+  if (B > INT32_MAX / H) return FA_ERR_SHAPE;
+  const int64_t bh = B * H;
+  const int64_t q_tiles = (N + rows - 1) / rows;
+  if (bh > INT32_MAX / q_tiles) return FA_ERR_SHAPE;
+
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return FA_ERR_ALIGN;
+  const uint64_t in_bytes = static_cast<uint64_t>(bh) * N * d * 2;
+  const uint64_t lse_bytes = static_cast<uint64_t>(bh) * N * 4;
+  if (overlaps(o, in_bytes, q, in_bytes) || overlaps(o, in_bytes, k, in_bytes) ||
+      overlaps(o, in_bytes, v, in_bytes) || overlaps(lse, lse_bytes, q, in_bytes) ||
+      overlaps(lse, lse_bytes, k, in_bytes) || overlaps(lse, lse_bytes, v, in_bytes) ||
+      overlaps(o, in_bytes, lse, lse_bytes))
+    return FA_ERR_ALIAS;
+
+  a->q = q;
+  a->k = k;
+  a->v = v;
+  a->o = o;
+  a->lse = lse;
+  a->bh = static_cast<int>(bh);
+  a->n = static_cast<int>(N);
+  a->q_tiles = static_cast<int>(q_tiles);
+  a->grid = static_cast<int>(bh * q_tiles);
+  a->xcd_grouped = (bh % 8 == 0) ? 1 : 0;
+  a->scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634074);
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" int flash_attn_fwd_validate(const void* q, const void* k, const void* v, void* o, float* lse,
+                                       int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
+                                       void* /*stream*/, int dtype) {
+  fa::FwdArgs a;
+  bool empty;
+  return check_args(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, &a, &empty);
+}
+
+extern "C" int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
+                              void* stream, int dtype) {
+  fa::FwdArgs a;
+  bool empty;
+  const int st = check_args(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, &a, &empty);
+  if (st != FA_OK || empty) return st;
+  const hipError_t err = fa::launch_fwd(a, dtype == FA_FP16, static_cast<int>(d), causal == 1,
+                                        static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}

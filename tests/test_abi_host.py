@@ -1,0 +1,128 @@
+"""The C-ABI library on the host: it loads, exports what the header declares, and
+rejects bad arguments before touching the GPU.
+
+No kernel is launched here. Acceptance checks go through flash_attn_fwd_validate
+(which never launches); flash_attn_fwd itself is only called with arguments that
+fail validation or describe an empty problem, both of which return before any
+HIP call. Fake addresses are never dereferenced.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import exact_attention_flash_amd as fa
+from exact_attention_flash_amd import _native
+from exact_attention_flash_amd.build import LIB_PATH
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flash_attn.h")
+
+A = 0x10000000          # 16-byte aligned fake device addresses, 1 GiB apart
+GB = 1 << 30
+SMALL = 16 * 64 * 2     # bytes of one [1,1,16,64] 16-bit tensor
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(flash_attn_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_loads_and_exports_header_symbols():
+    assert os.path.exists(LIB_PATH), "build the library first (__graft_entry__.build())"
+    names = _declared_functions()
+    assert names == ["flash_attn_abi_version", "flash_attn_fwd", "flash_attn_fwd_validate", "flash_attn_strerror"]
+    lib = ctypes.CDLL(LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n)
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (flash_attn_\w+)$", out, flags=re.M))
+    assert exported == set(names)
+
+
+def test_abi_version_and_strerror():
+    assert fa.flash_attn_abi_version() == 1
+    codes = [fa.FA_OK, fa.FA_ERR_NULL, fa.FA_ERR_SHAPE, fa.FA_ERR_HEADDIM, fa.FA_ERR_DTYPE,
+             fa.FA_ERR_SCALE, fa.FA_ERR_ALIGN, fa.FA_ERR_ALIAS, fa.FA_ERR_HIP, fa.FA_ERR_ARG]
+    msgs = [fa.flash_attn_strerror(c) for c in codes]
+    assert len(set(msgs)) == len(codes)
+    assert fa.flash_attn_strerror(12345) == "unknown status"
+
+
+def _args(q=A, k=A + GB, v=A + 2 * GB, o=A + 3 * GB, lse=A + 4 * GB, B=1, H=1, N=16, d=64,
+          causal=0, scale=0.125, stream=None, dtype=0):
+    return (q, k, v, o, lse, B, H, N, d, causal, scale, stream, dtype)
+
+
+BAD = [
+    (dict(B=-1), fa.FA_ERR_SHAPE), (dict(H=-2), fa.FA_ERR_SHAPE), (dict(N=-5), fa.FA_ERR_SHAPE),
+    (dict(d=32), fa.FA_ERR_HEADDIM), (dict(d=96), fa.FA_ERR_HEADDIM), (dict(d=256), fa.FA_ERR_HEADDIM),
+    (dict(dtype=2), fa.FA_ERR_DTYPE), (dict(dtype=-1), fa.FA_ERR_DTYPE),
+    (dict(causal=2), fa.FA_ERR_ARG), (dict(causal=-1), fa.FA_ERR_ARG),
+    (dict(scale=0.0), fa.FA_ERR_SCALE), (dict(scale=-0.5), fa.FA_ERR_SCALE),
+    (dict(scale=float("nan")), fa.FA_ERR_SCALE), (dict(scale=float("inf")), fa.FA_ERR_SCALE),
+    (dict(q=None), fa.FA_ERR_NULL), (dict(k=None), fa.FA_ERR_NULL), (dict(v=None), fa.FA_ERR_NULL),
+    (dict(o=None), fa.FA_ERR_NULL), (dict(lse=None), fa.FA_ERR_NULL),
+    (dict(q=A + 8), fa.FA_ERR_ALIGN), (dict(v=A + 2 * GB + 4), fa.FA_ERR_ALIGN),
+    (dict(o=A + 3 * GB + 2), fa.FA_ERR_ALIGN), (dict(lse=A + 4 * GB + 2), fa.FA_ERR_ALIGN),
+    (dict(o=A), fa.FA_ERR_ALIAS), (dict(o=A + GB + SMALL - 16), fa.FA_ERR_ALIAS),
+    (dict(o=A + 2 * GB - SMALL + 16), fa.FA_ERR_ALIAS),
+    (dict(lse=A + GB + 64), fa.FA_ERR_ALIAS), (dict(lse=A + 3 * GB + 64), fa.FA_ERR_ALIAS),
+    (dict(lse=A + 3 * GB - 60), fa.FA_ERR_ALIAS),
+    (dict(N=1 << 24, d=128), fa.FA_ERR_SHAPE), (dict(B=1 << 20, H=1 << 20, N=1 << 10), fa.FA_ERR_SHAPE),
+    (dict(B=1 << 40, H=1 << 40), fa.FA_ERR_SHAPE),
+]
+
+
+@pytest.mark.parametrize("kw,code", BAD)
+def test_validate_rejects(kw, code):
+    assert _native.validate_raw(*_args(**kw)) == code
+
+
+@pytest.mark.parametrize("kw,code", BAD)
+def test_fwd_rejects_before_launch(kw, code):
+    """flash_attn_fwd returns the same code and launches nothing."""
+    assert _native.fwd_raw(*_args(**kw)) == code
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(d=128, dtype=1, causal=1), dict(B=3, H=8, N=4099, d=128),
+                                dict(B=1, H=32, N=16384, d=128, causal=1)])
+def test_validate_accepts(kw):
+    size = kw.get("B", 1) * kw.get("H", 1) * kw.get("N", 16) * kw.get("d", 64) * 2
+    assert size < GB
+    assert _native.validate_raw(*_args(**kw)) == fa.FA_OK
+
+
+def test_adjacent_buffers_are_not_aliases():
+    # o right after v's last byte and lse right after o's last byte
+    args = _args(o=A + 2 * GB + SMALL, lse=A + 2 * GB + 2 * SMALL)
+    assert _native.validate_raw(*args) == fa.FA_OK
+
+
+def test_inputs_may_alias_each_other():
+    """q, k and v are read-only, so attention over a single buffer is allowed."""
+    assert _native.validate_raw(*_args(q=A, k=A, v=A)) == fa.FA_OK
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0)])
+def test_empty_problem_is_a_noop_even_with_null_pointers(kw):
+    args = _args(q=None, k=None, v=None, o=None, lse=None, **kw)
+    assert _native.validate_raw(*args) == fa.FA_OK
+    assert _native.fwd_raw(*args) == fa.FA_OK
+
+
+def test_python_binding_rejects_bad_tensors_before_the_library():
+    import torch
+
+    q = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.forward(q, q, q)                                   # CPU tensors
+    with pytest.raises(ValueError):
+        fa.forward(q[0], q[0], q[0])                          # not 4-D
+    with pytest.raises(ValueError):
+        fa.forward(q, q.half(), q)                            # dtype mismatch
+    with pytest.raises(TypeError):
+        fa._dtype_code(q.float())                             # fp32 is not a kernel dtype

@@ -69,3 +69,19 @@ def test_materialised_score_sizes_printed_by_the_pages():
         size = n * n * bpe * heads
         div = {"MiB": 2**20, "MB": 1e6, "GB": 1e9}[unit]
         assert round(size / div, 2) == value
+
+
+def test_half_ulp_of_output_dtypes():
+    from tests._parity import half_ulp
+
+    assert half_ulp(1.0, inputs.BF16) == 2.0**-8 and half_ulp(1.99, inputs.BF16) == 2.0**-8
+    assert half_ulp(2.0, inputs.BF16) == 2.0**-7 and half_ulp(-3.5, inputs.BF16) == 2.0**-7
+    assert half_ulp(47.0, inputs.FP16) == 2.0**-6 and half_ulp(1.0, inputs.FP16) == 2.0**-11
+    assert half_ulp(0.0, inputs.FP16) == 2.0**-25 and half_ulp(1e-6, inputs.FP16) == 2.0**-25
+    # every representable neighbour pair is exactly two half-ulps apart
+    for dt in inputs.DTYPES:
+        x = np.float32([0.3, 1.7, 9.1, 47.2])
+        b = inputs.to_bits(x, dt)
+        lo = inputs.bits_to_f64(b, dt)
+        hi = inputs.bits_to_f64(b + 1, dt)
+        assert np.allclose(hi - lo, 2 * half_ulp(lo, dt), rtol=0, atol=0)

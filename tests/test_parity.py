@@ -1,0 +1,212 @@
+"""GPU parity: the HIP kernels behind the C ABI against the float64 oracle.
+
+Every case draws seeded inputs (exact_attention_flash_amd.inputs), runs
+flash_attn_fwd on the GPU through the C ABI (via the thin Python binding), widens
+the 16-bit outputs exactly and compares element by element with oracle.dense on
+the same bytes, with the tolerances of tests/_parity.py.
+
+* Small shapes: full outputs, sizes that span several 128-row query tiles and
+  64-row key tiles, with ragged tails, N = 1 and N = 3, both dtypes, both masks.
+* The five workloads at full size, in the same launch configuration the
+  benchmark times: complete outputs where the oracle is quick (the 256- and
+  1024-token workloads) and otherwise sampled rows of every (batch, head) --
+  first/last rows, tile and wave boundaries, the ragged end and random rows --
+  plus complete heads; each with the workload seed and seed + 100.
+* Properties: the worked example of the tokenlab note zero-padded to d = 64,
+  V = 1, Q = 0, the causal prefix property (bitwise), determinism, a side stream,
+  empty problems and very large logits.
+"""
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import pytest
+
+from exact_attention_flash_amd import inputs
+from oracle.dense import attention as oracle_attention
+from tests import _golden
+from tests._parity import assert_parity, half_ulp, metrics
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def fa():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import exact_attention_flash_amd as fa_mod
+
+    fa_mod._native.lib()  # raises if the HIP library is not built
+    return fa_mod
+
+
+def _run_gpu(fa, qb, kb, vb, dtype, causal, scale, stream=None):
+    dev = torch.device("cuda:0")
+    q, k, v = (inputs.to_torch(x, dtype, dev) for x in (qb, kb, vb))
+    o, lse = fa.forward(q, k, v, causal=causal, scale=scale, stream=stream)
+    torch.cuda.synchronize()
+    return inputs.bits_to_f64(inputs.from_torch_bits(o), dtype), lse.double().cpu().numpy()
+
+
+def _oracle(qb, kb, vb, dtype, causal, scale, rows=None, heads=None):
+    if heads is not None:  # select (batch, head) slices before widening to float64
+        qb, kb, vb = (x.reshape(-1, *x.shape[-2:])[heads] for x in (qb, kb, vb))
+    q, k, v = (inputs.bits_to_f64(x, dtype) for x in (qb, kb, vb))
+    return oracle_attention(q, k, v, scale, causal=causal, rows=rows)
+
+
+SMALL_SHAPES = [(1, 1, 1, 64), (1, 1, 3, 128), (1, 2, 63, 64), (1, 1, 64, 128), (2, 3, 130, 64),
+                (1, 2, 200, 128), (1, 1, 257, 128), (2, 2, 384, 64), (1, 1, 511, 128)]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", [inputs.BF16, inputs.FP16])
+@pytest.mark.parametrize("shape", SMALL_SHAPES)
+def test_small_shapes_full(fa, shape, dtype, causal):
+    seed = 1000 + 7 * SMALL_SHAPES.index(shape) + (3 if causal else 0) + (1 if dtype == inputs.FP16 else 0)
+    qb, kb, vb = inputs.draw_qkv(shape, dtype, 1.0, seed)
+    scale = inputs.default_scale(shape[-1])
+    o, lse = _run_gpu(fa, qb, kb, vb, dtype, causal, scale)
+    ro, rl = _oracle(qb, kb, vb, dtype, causal, scale)
+    m = metrics(o, lse, ro, rl, dtype)
+    _log(f"small {shape} {dtype} causal={causal}: {m}")
+    assert_parity(m, f"{shape} {dtype} causal={causal}")
+
+
+def _sample_rows(n, count, rng):
+    fixed = [0, 1, 31, 32, 63, 64, 95, 127, 128, 129, 255, 256, n // 2, n - 129, n - 128, n - 65, n - 64,
+             n - 33, n - 32, n - 2, n - 1]
+    rows = set(r for r in fixed if 0 <= r < n)
+    rows.update(rng.integers(0, n, size=count).tolist())
+    return np.array(sorted(rows))
+
+
+CASES = [(name, c) for name, w in inputs.WORKLOADS.items() for c in w.causal]
+
+
+@pytest.mark.parametrize("seed_offset", [0, 100])
+@pytest.mark.parametrize("name,causal", CASES)
+def test_workload_parity(fa, name, causal, seed_offset):
+    w = inputs.WORKLOADS[name]
+    t0 = time.time()
+    qb, kb, vb = inputs.workload_qkv(w, seed_offset)
+    scale = inputs.default_scale(w.d)
+    _log(f"workload {name} causal={causal} seed={w.seed + seed_offset}: inputs ready {time.time() - t0:.1f}s")
+    o, lse = _run_gpu(fa, qb, kb, vb, w.dtype, causal, scale)
+    bh = w.B * w.H
+    o = o.reshape(bh, w.N, w.d)
+    lse = lse.reshape(bh, w.N)
+    _log(f"  gpu done {time.time() - t0:.1f}s")
+    if w.N * w.N * bh <= 1024 * 1024 * 64:
+        ro, rl = _oracle(qb, kb, vb, w.dtype, causal, scale)
+        m = metrics(o, lse, ro.reshape(bh, w.N, w.d), rl.reshape(bh, w.N), w.dtype)
+        _log(f"  full oracle {time.time() - t0:.1f}s: {m}")
+        assert_parity(m, name)
+        return
+    rng = np.random.default_rng(w.seed + seed_offset)
+    rows = _sample_rows(w.N, 24, rng)
+    go, gl, ro_all, rl_all = [], [], [], []
+    for h in range(bh):
+        ro, rl = _oracle(qb, kb, vb, w.dtype, causal, scale, rows=rows, heads=[h])
+        go.append(o[h, rows])
+        gl.append(lse[h, rows])
+        ro_all.append(ro[0])
+        rl_all.append(rl[0])
+    m = metrics(np.stack(go), np.stack(gl), np.stack(ro_all), np.stack(rl_all), w.dtype)
+    _log(f"  sampled {len(rows)} rows x {bh} slices {time.time() - t0:.1f}s: {m}")
+    assert_parity(m, f"{name} sampled rows")
+    # complete heads: first and last (batch, head) slice when the oracle is quick enough
+    full_heads = [0, bh - 1] if w.N <= 4099 else []
+    for h in full_heads:
+        ro, rl = _oracle(qb, kb, vb, w.dtype, causal, scale, heads=[h])
+        m = metrics(o[h], lse[h], ro[0], rl[0], w.dtype)
+        _log(f"  full slice {h} {time.time() - t0:.1f}s: {m}")
+        assert_parity(m, f"{name} slice {h}")
+
+
+@pytest.mark.parametrize("dtype", [inputs.BF16, inputs.FP16])
+def test_worked_example_padded(fa, dtype):
+    """Scores [2,1,0] and values [1,3,5] (tokenlab note), as d = 64 with zeros elsewhere."""
+    g = _golden.worked_example()
+    n, d = 3, 64
+    q = np.zeros((1, 1, n, d), np.float32)
+    k = np.zeros_like(q)
+    v = np.zeros_like(q)
+    q[..., 0] = 1.0
+    k[0, 0, :, 0] = g["scores"]
+    v[0, 0, :, 0] = g["values"]
+    qb, kb, vb = (inputs.to_bits(x, dtype) for x in (q, k, v))
+    o, lse = _run_gpu(fa, qb, kb, vb, dtype, False, 1.0)
+    # the printed value has 6 decimals; the output is that value rounded to the dtype
+    tol = half_ulp(g["u_over_l"], dtype) + 1e-5
+    assert np.all(np.abs(o[0, 0, :, 0] - g["u_over_l"]) <= tol)
+    assert np.all(o[0, 0, :, 1:] == 0.0)
+    assert np.allclose(lse, math.log(math.exp(2) + math.exp(1) + 1), atol=1e-5)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_constant_values_and_zero_queries(fa, causal):
+    B, H, N, d = 1, 2, 300, 128
+    qb, kb, vb = inputs.draw_qkv((B, H, N, d), inputs.BF16, 1.0, 77)
+    ones = inputs.to_bits(np.ones((B, H, N, d), np.float32), inputs.BF16)
+    o, _ = _run_gpu(fa, qb, kb, ones, inputs.BF16, causal, inputs.default_scale(d))
+    assert np.all(np.abs(o - 1.0) <= 2.0 ** -7)   # sum of rounded weights over the fp32 sum
+    zeros = inputs.to_bits(np.zeros((B, H, N, d), np.float32), inputs.BF16)
+    o, lse = _run_gpu(fa, zeros, kb, vb, inputs.BF16, causal, inputs.default_scale(d))
+    v = inputs.bits_to_f64(vb, inputs.BF16)
+    cnt = (np.arange(N) + 1) if causal else np.full(N, N)
+    mean = (np.cumsum(v, axis=2) / cnt[:, None]) if causal else np.broadcast_to(v.mean(axis=2, keepdims=True), v.shape)
+    assert np.max(np.abs(o - mean)) <= 1e-2
+    assert np.max(np.abs(lse - np.log(cnt))) <= 1e-5
+
+
+def test_causal_prefix_is_bitwise_independent_of_later_rows(fa):
+    """Rows < 4096 of a causal N = 4099 problem equal the N = 4096 problem exactly."""
+    dtype = inputs.FP16
+    qb, kb, vb = inputs.draw_qkv((1, 2, 4099, 128), dtype, 8.0, 55)
+    o1, l1 = _run_gpu(fa, qb, kb, vb, dtype, True, inputs.default_scale(128))
+    o2, l2 = _run_gpu(fa, qb[:, :, :4096].copy(), kb[:, :, :4096].copy(), vb[:, :, :4096].copy(),
+                      dtype, True, inputs.default_scale(128))
+    assert np.array_equal(o1[:, :, :4096], o2) and np.array_equal(l1[:, :, :4096], l2)
+
+
+def test_deterministic_and_side_stream(fa):
+    w = inputs.WORKLOADS["mha_b4_h16_n1024_d64"]
+    qb, kb, vb = inputs.workload_qkv(w)
+    a = _run_gpu(fa, qb, kb, vb, w.dtype, False, inputs.default_scale(w.d))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        b = _run_gpu(fa, qb, kb, vb, w.dtype, False, inputs.default_scale(w.d), stream=s)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_empty_problem_touches_nothing(fa):
+    q = torch.empty((2, 3, 0, 64), dtype=torch.bfloat16, device="cuda:0")
+    o, lse = fa.forward(q, q, q)
+    torch.cuda.synchronize()
+    assert o.shape == (2, 3, 0, 64) and lse.shape == (2, 3, 0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_very_large_logits(fa, causal):
+    """Logits in the thousands: no overflow; the result follows the largest scores."""
+    B, H, N, d = 1, 2, 190, 64
+    dtype = inputs.FP16
+    qb, kb, vb = inputs.draw_qkv((B, H, N, d), dtype, 8.0, 91)
+    scale = 2.0
+    o, lse = _run_gpu(fa, qb, kb, vb, dtype, causal, scale)
+    ro, rl = _oracle(qb, kb, vb, dtype, causal, scale)
+    m = metrics(o, lse, ro, rl, dtype)
+    _log(f"large logits causal={causal}: {m}")
+    assert m["finite"]
+    # the scores reach ~1e4 in magnitude; the LSE bound is relative to them
+    assert np.max(np.abs(lse - rl) / np.maximum(1.0, np.abs(rl))) <= 1e-6
+    assert m["o_max_excess"] <= 1e-2 and m["o_mean_abs"] <= 1e-3
