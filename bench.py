@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact attention forward on one MI355X.
+
+One step = one flash_attn_fwd call (the whole forward: scores, online softmax,
+P V, O and LSE) on the LLaMA-7B-shaped causal workload B=2, H=32, N=4096,
+d=128, bf16, inputs resident in HBM. Prints one JSON line:
+
+* value: TFLOP/s with the metric's count 4*B*H*N^2*d / 2 (causal), over the
+  K timed steps bracketed by synchronisations;
+* roofline: the kernel's average launch time from HIP events recorded on the
+  stream it runs on, its algorithmic FLOPs per launch, and the fraction of the
+  MI355X dense bf16 MFMA peak (2.5 PFLOP/s); `traffic` is the HBM bytes per
+  launch measured by rocprofv3 counters for this exact kernel source, or null;
+* cpu_baseline: the float64 CPU oracle timed on a bounded sample of the same
+  workload (a few complete (batch, head) slices) on this host's cores.
+
+Options --workload and --all select other workloads (diagnostics; the JSON line
+keeps the headline workload by default).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA, vendor figure
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ["exact_attention_flash_amd/csrc/fwd_kernel.hip", "exact_attention_flash_amd/csrc/fwd_kernel.h"]
+TRAFFIC_FILE = "profiles/fwd_kernel_hbm_traffic.txt"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, causal: bool):
+    """HBM bytes per launch recorded for this kernel source, or None if stale/absent."""
+    path = os.path.join(ROOT, TRAFFIC_FILE)
+    if not os.path.exists(path):
+        return None
+    want = kernel_source_hash()
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            fields = dict(kv.split("=", 1) for kv in line.split())
+            if (fields.get("workload") == workload and fields.get("causal") == str(int(causal))
+                    and fields.get("source_sha256_16") == want):
+                return float(fields["hbm_bytes_per_launch"])
+    return None
+
+
+def time_gpu(w, causal, steps, warmup):
+    import torch
+
+    import exact_attention_flash_amd as fa
+    from exact_attention_flash_amd import inputs
+
+    dev = torch.device("cuda:0")
+    qb, kb, vb = inputs.workload_qkv(w)
+    q, k, v = (inputs.to_torch(x, w.dtype, dev) for x in (qb, kb, vb))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    scale = inputs.default_scale(w.d)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        fa.flash_attn_fwd(q, k, v, o, lse, causal=causal, scale=scale, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    mem0 = torch.cuda.memory_allocated(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
+
+    # per-launch HIP events on the kernel's stream: the distribution
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    per_launch = sorted(a.elapsed_time(b) for a, b in evs)
+
+    # the timed region of the contract: K back-to-back steps between synchronisations
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = e0.elapsed_time(e1) / steps
+    extra = torch.cuda.max_memory_allocated(dev) - mem0
+    return {
+        "wall_s": wall, "ms_per_step": wall * 1e3 / steps, "event_ms_per_launch": ev_ms,
+        "launch_ms_median": statistics.median(per_launch),
+        "launch_ms_p10": per_launch[int(0.1 * (len(per_launch) - 1))],
+        "launch_ms_p90": per_launch[int(0.9 * (len(per_launch) - 1))],
+        "extra_alloc_bytes": int(extra),
+        "device": torch.cuda.get_device_name(dev),
+    }, (qb, kb, vb)
+
+
+def cpu_baseline(w, causal, qkv_bits, slices):
+    """Time the float64 oracle on `slices` complete (batch, head) slices of the workload."""
+    import numpy as np
+
+    from exact_attention_flash_amd import inputs
+    from oracle.dense import attention
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas_threads = max((p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"),
+                           default=1)
+    except Exception:  # noqa: BLE001 - reporting only
+        blas_threads = None
+    cores = len(os.sched_getaffinity(0))
+    qb, kb, vb = (x.reshape(-1, w.N, w.d)[:slices] for x in qkv_bits)
+    q, k, v = (inputs.bits_to_f64(x, w.dtype) for x in (qb, kb, vb))
+    t0 = time.perf_counter()
+    attention(q, k, v, inputs.default_scale(w.d), causal=causal)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * slices * w.N * w.N * w.d / (2.0 if causal else 1.0)
+    _ = np
+    return {
+        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads or cores, "kind": "oracle",
+        "sample": f"{slices} of {w.B * w.H} (batch, head) slices of the same workload, all {w.N} rows, "
+                  f"float64 numpy (BLAS matmuls, {blas_threads} BLAS threads on {cores} host cores); "
+                  f"{dt:.1f} s, scaled with the same FLOP formula",
+        "seconds": dt,
+    }
+
+
+def copy_calibration(mib, reps):
+    """A plain copy kernel of known size: reads and writes MIB MiB per launch."""
+    import torch
+
+    n = mib * (1 << 20) // 4
+    src = torch.arange(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    print(json.dumps({"copy_mib": mib, "bytes_read": n * 4, "bytes_written": n * 4, "ms_per_copy": ms,
+                      "GB_per_s": 2 * n * 4 / (ms * 1e-3) / 1e9}), flush=True)
+
+
+def run(args, workload_name, causal):
+    from exact_attention_flash_amd import inputs
+
+    w = inputs.WORKLOADS[workload_name]
+    flops = w.flops(causal)
+    g, qkv = time_gpu(w, causal, args.steps, args.warmup)
+    tflops = flops / (g["ms_per_step"] * 1e-3) / 1e12
+    achieved = flops / (g["event_ms_per_launch"] * 1e-3) / 1e12
+    traffic = measured_traffic(workload_name, causal)
+    line = {
+        "metric": "attention fwd TFLOP/s and % of bf16 MFMA peak, N=4096 d=128 causal",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(g["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": causal,
+                   "dtype": w.dtype, "sigma": w.sigma, "seed": w.seed, "parallelism": "single GPU"},
+        "roofline": {
+            "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel": "fwd_kernel (flash_attn_fwd)",
+            "flop_per_launch": flops,
+            "launch_ms": round(g["event_ms_per_launch"], 5),
+            "launch_ms_median": round(g["launch_ms_median"], 5),
+            "launch_ms_p10": round(g["launch_ms_p10"], 5),
+            "launch_ms_p90": round(g["launch_ms_p90"], 5),
+            "compulsory_hbm_bytes": w.compulsory_bytes(),
+        },
+        "extra_alloc_bytes": g["extra_alloc_bytes"],
+        "device": g["device"],
+        "kernel_source_sha256_16": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, causal, qkv, args.cpu_slices)
+    return line
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=None, help="workload name (default: the LLaMA-7B causal one)")
+    ap.add_argument("--causal", type=int, default=None, help="override the mask for --workload (0/1)")
+    ap.add_argument("--all", action="store_true", help="one line per workload and mask (diagnostics)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-slices", type=int, default=64, help="(batch, head) slices the oracle times")
+    ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
+                    help="only run plain device-to-device copies of MIB MiB (HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the forward pass shards over (batch, head) with no communication; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+    if os.environ.get("WORLD_SIZE", "1") != "1":
+        print("bench.py: launched with WORLD_SIZE > 1; only one GPU is supported", file=sys.stderr)
+        sys.exit(2)
+
+    if args.copy_calib:
+        copy_calibration(args.copy_calib, args.steps)
+        return
+
+    from exact_attention_flash_amd import inputs
+
+    if args.all:
+        for name, w in inputs.WORKLOADS.items():
+            for c in w.causal:
+                args2 = argparse.Namespace(**vars(args))
+                args2.no_cpu_baseline = True
+                print(json.dumps(run(args2, name, c)), flush=True)
+        return
+    name = args.workload or inputs.HEADLINE
+    causal = inputs.WORKLOADS[name].causal[0] if args.causal is None else bool(args.causal)
+    print(json.dumps(run(args, name, causal)), flush=True)
+
+
+if __name__ == "__main__":
+    main()

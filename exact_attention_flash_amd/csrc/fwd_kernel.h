@@ -1,4 +1,4 @@
-// Internal interface between the C ABI layer and the gfx950 forward kernels.
+// Internal interface between the C ABI layer and the gfx950 forward kernel.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>

@@ -1,44 +1,56 @@
 // Exact attention forward for gfx950 (MI355X): bf16/fp16 in, fp32 accumulate.
 //
 // Method ("FlashAttention: optimize data movement before counting FLOPs",
-// section 02): for each key tile with scores s and values V keep the running row
+// section 02): per key tile with scores s and values V, keep the running row
 // maximum m, denominator l and unnormalised numerator u,
 //     m' = max(m, max s),  l' = e^(m-m') l + sum e^(s-m'),  u' = e^(m-m') u + sum e^(s-m') V,
-// and finish with O = u / l. The loop order is the one the IO-aware survey
-// ("FlashAttention: IO-Aware Tiling, Online Softmax Mathematics, Memory Hierarchy
-// Dynamics, and Kernel Evolution", FlashAttention-2 section) describes: query
-// tiles on the grid, key/value tiles streamed in the inner loop, the accumulator
-// kept on chip and divided once at the end. The log-sum-exp m + ln l is stored
-// for a backward pass (same survey, "Backward Pass Recomputation").
+// and finish with O = u / l and LSE = m + ln l ("FlashAttention: IO-Aware Tiling,
+// Online Softmax Mathematics, Memory Hierarchy Dynamics, and Kernel Evolution",
+// sections on FlashAttention-2 and on backward recomputation). Query tiles sit on
+// the grid, key/value tiles stream through LDS, the accumulator stays in registers
+// and is divided once at the end.
 //
-// gfx950 mapping (one workgroup = 4 wave64s = 128 query rows; one key tile = 64 rows):
-//  * Each wave owns 32 query rows. Scores are computed transposed, S^T = K Q^T,
-//    with v_mfma_f32_32x32x16 (A = K rows from LDS, B = the wave's Q rows held in
-//    registers). In the 32x32 accumulator layout a lane holds one query column
-//    and 16 key rows, so the row max and row sum are mostly in-lane; the two
-//    32-lane halves that share a query are combined with v_permlane32_swap.
-//  * The probabilities stay in registers: the S^T accumulator, rounded to the
-//    16-bit input type, is exactly the B operand of O^T = V^T P^T. The V^T
-//    operand is read from a row-major V tile with ds_read_b64_tr_b16 (gfx950's
-//    transposing LDS read), so no transpose pass is needed anywhere.
-//  * O^T accumulates in registers: each lane owns one query, so the rescale by
-//    e^(m-m') is a per-lane multiply, skipped when no row of the wave moved its max.
+// Workgroup: 8 wave64s, 256 query rows, 64-key tiles.
+//  * Each wave owns 32 query rows and computes S^T = K Q^T and O^T = V^T P^T with
+//    v_mfma_f32_32x32x16 (bf16 or fp16 in, fp32 out). In the 32x32 accumulator
+//    layout a lane holds one query and 16 keys, so row max and row sum are in-lane
+//    plus one v_permlane32_swap, and the S^T accumulator rounded to 16 bits is the
+//    B operand of the P V product without leaving registers. V^T is read from the
+//    row-major V tile with ds_read_b64_tr_b16.
+//  * Ping-pong: waves 0-3 (group A) and 4-7 (group B) land on the four SIMDs in
+//    pairs. Every iteration has two barrier-separated slots; in each slot one
+//    group issues its matrix work (S of tile i and P V of tile i-1) while the other
+//    runs the softmax of its latest scores on the vector ALU, so MFMA and VALU work
+//    of the two waves sharing a SIMD overlap.
+//  * K/V tiles are loaded straight into LDS with buffer_load ... lds (no staging
+//    registers) into a 4-stage ring, two tiles ahead of use. Rows past the end of
+//    the sequence read as zeros through the buffer descriptor's range. The tiles
+//    are stored unpadded with 16-byte chunks XOR-swizzled by row, chosen so that
+//    the K reads (16 lanes, 16 rows) and the transposing V reads (32 lanes, 4 rows)
+//    hit every LDS bank once.
+//  * Group A owns row blocks 0,2,4,6 and group B blocks 1,3,5,7, so under a causal
+//    mask both groups visit the same number of key tiles.
 //  * Exponentials use exp2 with scale*log2(e) folded into one FMA per score.
-//  * K/V tiles are double-buffered in LDS; the next tile is fetched into
-//    registers while the current one is consumed; one barrier per tile.
-//  * Causal: key tiles past the workgroup's last row are never visited, waves
-//    whose rows all precede a tile skip its math, and only tiles that straddle
-//    the diagonal or the end of the sequence evaluate the mask.
-//  * Workgroup order: heaviest causal query tiles first, and all query tiles of
-//    one (batch, head) on the same XCD (workgroups go round-robin over 8 XCDs)
-//    so that K/V tiles are shared through that XCD's L2.
+//  * Causal: tiles past the workgroup's last row are never loaded; waves skip the
+//    math of tiles entirely after their rows; only tiles on the diagonal or at the
+//    end of the sequence evaluate the mask.
+//  * Workgroup order: heaviest causal query tiles first; all query tiles of one
+//    (batch, head) on one XCD so K/V tiles are shared through its L2.
+//
+// Reference maximum: with TAU = 0 the reference is the running maximum. With TAU
+// > 0 (log2 units) a row keeps its reference until a tile's maximum exceeds it by
+// more than TAU; the rescaling identity of "6.1 FlashAttention V1 in detail", §3.3
+// holds for any reference, so u / l and m + ln l are unchanged, and exponent
+// arguments stay <= TAU (probabilities <= 2^TAU).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "fwd_kernel.h"
 
 namespace fa {
-namespace {
+namespace pp {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -50,54 +62,59 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 4;
-constexpr int kBM = 32 * kWaves;  // query rows per workgroup
-constexpr int kBN = 64;           // key rows per tile
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
+constexpr int kBM = 32 * kWaves;  // query rows per workgroup
+constexpr int kBN = 64;           // keys per tile
+constexpr int kStages = 4;        // LDS ring depth (tiles)
+constexpr int kAhead = kStages - 2;  // tiles in flight ahead of use
+constexpr uint32_t kBufferConfig = 0x00020000u;  // raw buffer descriptor word 3 (gfx9 family)
+
+// Reference-maximum slack in log2 units (see the header comment); 0 rescales
+// whenever a row maximum rises. 0 is the default: it keeps the dominant
+// probability of every row at exactly 2^0 = 1, which 16-bit P represents
+// exactly; with a slack the dominant term becomes 2^x, 0 < x <= TAU, and its
+// rounding to 16 bits reaches the output at about 2^-11 (fp16) of |O|.
+#ifndef FA_RESCALE_TAU
+#define FA_RESCALE_TAU 0
+#endif
 
 template <int D>
-struct Layout {
-  // LDS row strides in bytes. K rows (read 16 bytes per lane, 32 rows per
-  // instruction) are padded by 16 bytes so consecutive rows start 4 banks apart.
-  // V rows (read 8 bytes per lane by the transposing read, 4 rows x 16 dwords
-  // per half-wave) are padded so those 4 rows land in disjoint 16-bank windows.
-  static constexpr int kStride = D * 2 + 16;
-  static constexpr int vStride = D * 2 + 64;
-  static constexpr int kBytes = kBN * kStride;
-  static constexpr int vBytes = kBN * vStride;
-  static constexpr int stageBytes = kBytes + vBytes;
-  static constexpr int chunksPerRow = D / 8;                 // 16-byte chunks
-  static constexpr int chunksPerThread = kBN * chunksPerRow / kThreads;
-  static_assert(kBN * chunksPerRow % kThreads == 0, "tile load must split evenly");
+struct Geo {
+  static constexpr int rowBytes = D * 2;
+  static constexpr int chunksPerRow = D / 8;  // 16-byte chunks
+  static constexpr int tileBytes = kBN * rowBytes;
+  static constexpr int stageBytes = 2 * tileBytes;  // K then V
+  static constexpr int blocksPerTile = tileBytes / 1024;  // 1 KiB per wave-instruction
+  static constexpr int loadsPerWave = 2 * blocksPerTile / kWaves;  // K + V instructions per wave per tile
+  static_assert(blocksPerTile % kWaves == 0, "tile must split into whole 1 KiB blocks per wave");
+  // XOR swizzle of the 16-byte chunk index within a row
+  __device__ static __forceinline__ int swz(int row) {
+    if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+    else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+  }
 };
 
 template <bool FP16>
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
   if constexpr (FP16) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                  0, 0, 0);
   } else {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
   }
 }
 
-// Two fp32 values rounded to nearest-even 16-bit floats, packed low|high
-// (one v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32).
 template <bool FP16>
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   const f32x2 v = {lo, hi};
-  if constexpr (FP16) {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
-  } else {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-  }
+  if constexpr (FP16) return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+  else return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-// Value of x held by the lane 32 positions away (the other half of the wave).
 __device__ __forceinline__ float other_half(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  // lanes 0..31 receive the upper half's value in r[1]; lanes 32..63 in r[0]
   return (threadIdx.x & 32) ? __uint_as_float(r[0]) : __uint_as_float(r[1]);
 }
 
@@ -106,27 +123,53 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
   return __builtin_bit_cast(u32x2, r);
 }
 
-__device__ __forceinline__ u32x4 lds_read16(const char* p) {
-  return *reinterpret_cast<const u32x4*>(p);
+__device__ __forceinline__ u32x4 lds_read16(const char* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kBufferConfig);
+}
+
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+// 16 bytes per lane from the buffer straight into LDS at lds_base + 16 * lane
+// (buffer_load_dwordx4 ... lds; M0 holds the wave-uniform LDS base). Written as
+// inline assembly so that the compiler does not treat every later LDS read as
+// possibly aliasing the in-flight copy (it would then wait for all outstanding
+// loads, tiles prefetched for later iterations included); completion is instead
+// awaited explicitly with wait_vmcnt before the barrier that publishes a tile.
+__device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, uint32_t off, char* lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)lds_base));
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(m0) : "memory");
+}
+
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: expcnt and lgkmcnt at max).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
 template <bool FP16, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
-  using L = Layout<D>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * L::stageBytes];
+__global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
+  using G = Geo<D>;
+  __shared__ __attribute__((aligned(1024))) char smem[kStages * G::stageBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int h = lane >> 5;    // which half of the wave
-  const int l32 = lane & 31;  // query column within the wave's 32
+  const int grp = wave >> 2;  // 0: group A, 1: group B
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
 
   // ---- workgroup -> (batch*head, query tile) ----
   const int bid = blockIdx.x;
   const int bh_count = a.bh;
   int bh, rank;
   if (a.xcd_grouped) {
-    const int hpx = bh_count / 8;  // heads per XCD
+    const int hpx = bh_count / 8;
     const int xcd = bid & 7, t = bid >> 3;
     rank = t / hpx;
     bh = xcd * hpx + t % hpx;
@@ -138,161 +181,215 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
   const int N = a.n;
   const int q0 = qtile * kBM;
   const int64_t head_off = (int64_t)bh * N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const uint16_t* qg = reinterpret_cast<const uint16_t*>(a.q) + head_off;
+  const uint16_t* kg = reinterpret_cast<const uint16_t*>(a.k) + head_off;
+  const uint16_t* vg = reinterpret_cast<const uint16_t*>(a.v) + head_off;
 
-  const uint16_t* __restrict__ qg = reinterpret_cast<const uint16_t*>(a.q) + head_off;
-  const uint16_t* __restrict__ kg = reinterpret_cast<const uint16_t*>(a.k) + head_off;
-  const uint16_t* __restrict__ vg = reinterpret_cast<const uint16_t*>(a.v) + head_off;
+  // rows of this wave: block 2*(wave%4) + grp of the workgroup's 8 blocks of 32
+  const int row0 = q0 + 32 * (2 * (wave & 3) + grp);
+  const int qrow = row0 + l32;
 
-  // ---- Q rows of this lane's query, as B operands (k-slots d = 16*ks + 8*h + 0..7) ----
-  const int qrow = q0 + wave * 32 + l32;
+  // ---- tiles visited by the workgroup ----
+  const int tiles_all = (N + kBN - 1) / kBN;
+  int n_tiles = tiles_all;
+  if (CAUSAL) n_tiles = min(tiles_all, (min(q0 + kBM, N) - 1) / kBN + 1);
+
+  // ---- direct-to-LDS tile loads: this wave fills blocks wave + 8*i of K and of V ----
+  // lane `lane` of block b lands at chunk position 64*b + lane = (row, physical chunk);
+  // it fetches the logical chunk physical ^ swz(row) of that row.
+  uint32_t ld_off[G::blocksPerTile / kWaves];
+#pragma unroll
+  for (int i = 0; i < G::blocksPerTile / kWaves; ++i) {
+    const int p = 64 * (wave + kWaves * i) + lane;
+    const int row = p / G::chunksPerRow, phys = p % G::chunksPerRow;
+    ld_off[i] = (uint32_t)row * G::rowBytes + (uint32_t)((phys ^ G::swz(row)) * 16);
+  }
+  auto issue_tile = [&](int t) {
+    const uint32_t skip = (uint32_t)t * kBN * G::rowBytes;
+    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(kg + (int64_t)t * kBN * D, head_bytes - skip);
+    const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(vg + (int64_t)t * kBN * D, head_bytes - skip);
+    char* st = smem + (t % kStages) * G::stageBytes;
+#pragma unroll
+    for (int i = 0; i < G::blocksPerTile / kWaves; ++i) {
+      buffer_load16_lds(kr, ld_off[i], st + 1024 * (wave + kWaves * i));
+      buffer_load16_lds(vr, ld_off[i], st + G::tileBytes + 1024 * (wave + kWaves * i));
+    }
+  };
+
+  // prologue: the first kAhead tiles go in flight, then the Q rows of this lane's
+  // query (B operands, k-slots d = 16*kk + 8*h + 0..7); one wait covers all of them,
+  // so the compiler also sees the Q registers complete before the loop.
+  issue_tile(0);
+  if (n_tiles > 1) issue_tile(1);
   u32x4 qreg[D / 16];
+  {
+    const __amdgpu_buffer_rsrc_t qr = buffer_rsrc(qg, head_bytes);
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    qreg[ks] = (qrow < N) ? *reinterpret_cast<const u32x4*>(qg + (int64_t)qrow * D + ks * 16 + h * 8)
-                          : u32x4{0, 0, 0, 0};
+    for (int kk = 0; kk < D / 16; ++kk) qreg[kk] = buffer_load16(qr, (uint32_t)qrow * G::rowBytes + kk * 32 + h * 16);
   }
+  wait_vmcnt<0>();
+  __syncthreads();
 
-  // ---- key tiles this workgroup visits ----
-  const int kv_tiles_all = (N + kBN - 1) / kBN;
-  int n_tiles = kv_tiles_all;
-  if (CAUSAL) {
-    const int last_row = min(q0 + kBM, N) - 1;
-    n_tiles = min(kv_tiles_all, last_row / kBN + 1);
-  }
-  const int wave_first_row = q0 + wave * 32;
-  const int wave_last_row = wave_first_row + 31;
-
-  // global -> register staging of one K/V tile (16-byte chunks, coalesced rows)
-  u32x4 kstage[L::chunksPerThread], vstage[L::chunksPerThread];
-  auto fetch = [&](int tile) {
-    const int kv0 = tile * kBN;
+  // ---- per-lane LDS offsets (within a stage) ----
+  // K: row l32 (+32 for the second block of keys), logical chunk 2*kk + h
+  const int krow_sw = G::swz(l32);
+  const int k_lane = l32 * G::rowBytes;
+  // V (transposing read): source row 16t + 8*half + 4h + (lane%16)/4, logical chunk
+  // 4*db + 2*((lane/16)%2) + (lane%4)/2, byte 8*(lane%2) inside the chunk
+  const int vk = (lane & 15) >> 2;
+  const int vrow_base = 4 * h + vk;
+  int v_lane[2][D / 32];
 #pragma unroll
-    for (int i = 0; i < L::chunksPerThread; ++i) {
-      const int c = tid + i * kThreads;
-      const int row = c / L::chunksPerRow, col = (c % L::chunksPerRow) * 8;
-      const bool ok = kv0 + row < N;
-      const int64_t off = (int64_t)(kv0 + row) * D + col;
-      kstage[i] = ok ? *reinterpret_cast<const u32x4*>(kg + off) : u32x4{0, 0, 0, 0};
-      vstage[i] = ok ? *reinterpret_cast<const u32x4*>(vg + off) : u32x4{0, 0, 0, 0};
-    }
-  };
-  auto stash = [&](int buf) {
-    char* ks = smem + buf * L::stageBytes;
-    char* vs = ks + L::kBytes;
+  for (int half = 0; half < 2; ++half)
 #pragma unroll
-    for (int i = 0; i < L::chunksPerThread; ++i) {
-      const int c = tid + i * kThreads;
-      const int row = c / L::chunksPerRow, colb = (c % L::chunksPerRow) * 16;
-      *reinterpret_cast<u32x4*>(ks + row * L::kStride + colb) = kstage[i];
-      *reinterpret_cast<u32x4*>(vs + row * L::vStride + colb) = vstage[i];
+    for (int db = 0; db < D / 32; ++db) {
+      const int row = 8 * half + vrow_base;
+      const int logical = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+      v_lane[half][db] = row * G::rowBytes + ((logical ^ G::swz(row)) * 16) + 8 * (lane & 1);
     }
-  };
 
-  // per-lane offsets inside a stage
-  const int k_off = l32 * L::kStride + h * 16;  // K row l32 (+32 for the second block), d-slot 8h
-  // transposing V read: this lane sources row 4h + (lane%16)/4 (+8, +16t) and
-  // columns 16*((lane/16)%2) + 4*(lane%4) (+32 per d block)
-  const int v_off = (4 * h + ((lane & 15) >> 2)) * L::vStride + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
-
-  const float sc = a.scale_log2;  // scale * log2(e)
-  float m_run = -INFINITY;        // running max of scale*log2(e)*s for this lane's query
-  float l_run = 0.f;              // running denominator (this half's keys only)
+  const float sc = a.scale_log2;
+  float m_run = -INFINITY;  // reference maximum (log2 units) of this lane's query
+  float l_run = 0.f;        // denominator over this half-wave's keys
   f32x16 acc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
+  f32x16 s[2] = {f32x16{}, f32x16{}};
+  u32x4 pb[4] = {u32x4{}, u32x4{}, u32x4{}, u32x4{}};
 
-  if (n_tiles > 0) {
-    fetch(0);
-    stash(0);
-  }
-  __syncthreads();
+  const int wave_last_row = row0 + 31;
+  auto active = [&](int t) { return row0 < N && (!CAUSAL || t * kBN <= wave_last_row); };
 
-  for (int j = 0; j < n_tiles; ++j) {
-    const int buf = j & 1;
-    const bool more = j + 1 < n_tiles;
-    if (more) fetch(j + 1);
-
-    const int kv0 = j * kBN;
-    const bool active = wave_first_row < N && (!CAUSAL || kv0 <= wave_last_row);
-    if (active) {
-      const char* ks = smem + buf * L::stageBytes;
-      const char* vs = ks + L::kBytes;
-
-      // ---- S^T = K Q^T for 64 keys x 32 queries ----
-      f32x16 s[2] = {f32x16{}, f32x16{}};
+  // per-lane K offsets: row l32 (the second block of 32 keys adds 32 rows), logical
+  // chunk 2*kk + h
+  int k_off[D / 16];
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const u32x4 k0 = lds_read16(ks + k_off + kk * 32);
-        const u32x4 k1 = lds_read16(ks + k_off + 32 * L::kStride + kk * 32);
-        s[0] = mfma32<FP16>(k0, qreg[kk], s[0]);
-        s[1] = mfma32<FP16>(k1, qreg[kk], s[1]);
+  for (int kk = 0; kk < D / 16; ++kk) k_off[kk] = k_lane + (((2 * kk + h) ^ krow_sw) * 16);
+
+  // Matrix phase of tile i: S^T(i) = K_i Q^T (D/8 MFMAs) and u += P(i-1) V(i-1)
+  // (D/8 MFMAs), interleaved one for one. Operand reads from LDS are issued kLook
+  // steps ahead of their MFMA so that LDS latency hides behind matrix work; the
+  // scheduling fences keep the compiler from regrouping reads next to their uses.
+  constexpr int kSteps = D / 8;
+#ifdef FA_LOOKAHEAD
+  constexpr int kLook = FA_LOOKAHEAD;
+#else
+  constexpr int kLook = 3;
+#endif
+  auto mfma_steps = [&](auto do_s_c, auto do_p_c, int i) {
+    constexpr bool DO_S = decltype(do_s_c)::value;
+    constexpr bool DO_P = decltype(do_p_c)::value;
+    const char* kt = smem + (i % kStages) * G::stageBytes;
+    const char* vt = smem + ((i + kStages - 1) % kStages) * G::stageBytes + G::tileBytes;
+    u32x4 kop[kLook + 1];
+    u32x2 vlo[kLook + 1], vhi[kLook + 1];
+    auto issue = [&](int st) {
+      if constexpr (DO_S) kop[st % (kLook + 1)] = lds_read16(kt + k_off[st >> 1] + (st & 1) * 32 * G::rowBytes);
+      if constexpr (DO_P) {
+        const int t = st / (D / 32), db = st % (D / 32);
+        vlo[st % (kLook + 1)] = lds_read_tr16(vt + v_lane[0][db] + 16 * t * G::rowBytes);
+        vhi[st % (kLook + 1)] = lds_read_tr16(vt + v_lane[1][db] + 16 * t * G::rowBytes);
       }
-
-      // ---- mask keys past the end and (causal) keys after the query ----
-      const bool edge = (kv0 + kBN > N) || (CAUSAL && kv0 + kBN - 1 > wave_first_row);
-      if (edge) {
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kv0 + b * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            const bool dead = key >= N || (CAUSAL && key > qrow);
-            s[b][r] = dead ? -INFINITY : s[b][r];
-          }
-      }
-
-      // ---- running max (in log2 units) ----
-      float mx = s[0][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-      mx = fmaxf(mx, other_half(mx));
-      const float m_new = fmaxf(m_run, mx * sc);
-      const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;  // no -inf - -inf
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
-
-      // ---- p = 2^(s*sc - m'), partial row sum, 16-bit P operands ----
-      float psum = 0.f;
-      u32x4 pb[4];
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        float p[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], sc, -m_ref));
-          psum += p[r];
-        }
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          pb[2 * b + t2] = u32x4{pack2<FP16>(p[8 * t2 + 0], p[8 * t2 + 1]), pack2<FP16>(p[8 * t2 + 2], p[8 * t2 + 3]),
-                                 pack2<FP16>(p[8 * t2 + 4], p[8 * t2 + 5]), pack2<FP16>(p[8 * t2 + 6], p[8 * t2 + 7])};
-        }
-      }
-      l_run = alpha * l_run + psum;
-      m_run = m_new;
-
-      // ---- u <- alpha * u (skipped when no query of the wave raised its max) ----
-      if (__any(alpha != 1.0f)) {
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
-      }
-
-      // ---- u += P V: O^T = V^T P^T over 4 groups of 16 keys ----
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const char* p0 = vs + v_off + (16 * t) * L::vStride + db * 64;
-          const u32x2 lo = lds_read_tr16(p0);
-          const u32x2 hi = lds_read_tr16(p0 + 8 * L::vStride);
-          acc[db] = mfma32<FP16>(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[t], acc[db]);
-        }
-      }
+    };
+    if constexpr (DO_S) {
+      s[0] = f32x16{};
+      s[1] = f32x16{};
     }
+#pragma unroll
+    for (int st = 0; st < kLook; ++st) issue(st);
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st) {
+      if (st + kLook < kSteps) issue(st + kLook);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (DO_S) s[st & 1] = mfma32<FP16>(kop[st % (kLook + 1)], qreg[st >> 1], s[st & 1]);
+      if constexpr (DO_P) {
+        const int t = st / (D / 32), db = st % (D / 32);
+        const int slot = st % (kLook + 1);
+        acc[db] = mfma32<FP16>(u32x4{vlo[slot][0], vlo[slot][1], vhi[slot][0], vhi[slot][1]}, pb[t], acc[db]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto mfma_phase = [&](int i) {
+    const bool do_s = i < n_tiles && active(i);
+    const bool do_p = i >= 1 && active(i - 1);
+    if (do_s && do_p) mfma_steps(std::true_type{}, std::true_type{}, i);
+    else if (do_s) mfma_steps(std::true_type{}, std::false_type{}, i);
+    else if (do_p) mfma_steps(std::false_type{}, std::true_type{}, i);
+  };
 
-    if (more) stash(buf ^ 1);
+  // online softmax of S(t): reference max, p, l, rescale of u, 16-bit P. Max and
+  // sum run as four independent chains to keep the VALU pipeline full.
+  auto softmax_phase = [&](int t) {
+    if (!(t >= 0 && t < n_tiles && active(t))) return;
+    const int kv0 = t * kBN;
+    if ((kv0 + kBN > N) || (CAUSAL && kv0 + kBN - 1 > row0)) {
+      // key = kv0 + c(b, r) + 4h with c(b, r) = 32b + 8(r/4) + r%4; a key is dead
+      // past the sequence end or (causal) after the query: c(b, r) > lim
+      int lim = N - 1 - kv0;
+      if (CAUSAL) lim = min(lim, qrow - kv0);
+      lim -= 4 * h;
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[b][r] = (32 * b + 8 * (r >> 2) + (r & 3) > lim) ? -INFINITY : s[b][r];
+    }
+    float mc[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const f32x16& v = s[c >> 1];
+      const int o = 8 * (c & 1);
+      mc[c] = __builtin_fmaxf(__builtin_fmaxf(v[o], v[o + 1]), v[o + 2]);
+#pragma unroll
+      for (int r = 3; r < 8; ++r) mc[c] = __builtin_fmaxf(mc[c], v[o + r]);
+    }
+    float mx = __builtin_fmaxf(__builtin_fmaxf(mc[0], mc[1]), __builtin_fmaxf(mc[2], mc[3]));
+    mx = __builtin_fmaxf(mx, other_half(mx)) * sc;
+    const float m_new = (mx > m_run + (float)FA_RESCALE_TAU) ? mx : m_run;
+    const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
+    float ps[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const f32x16& v = s[c >> 1];
+      const int o = 8 * (c & 1);
+      float p[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[o + r], sc, -m_ref));
+      ps[c] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      pb[c] = u32x4{pack2<FP16>(p[0], p[1]), pack2<FP16>(p[2], p[3]), pack2<FP16>(p[4], p[5]),
+                    pack2<FP16>(p[6], p[7])};
+    }
+    l_run = alpha * l_run + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
+    m_run = m_new;
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
+    }
+  };
+
+  // tile i+1 must have landed (every wave waits for its own loads) before the
+  // barrier that precedes slot 2(i+1); tile i+kAhead may stay in flight.
+  auto wait_next = [&](int i) {
+    if (i + kAhead < n_tiles) wait_vmcnt<G::loadsPerWave>();
+    else wait_vmcnt<0>();
+  };
+
+  for (int i = 0; i <= n_tiles; ++i) {
+    // refill the stage last used by tile i-2 with tile i+kAhead
+    if (i + kAhead < n_tiles) issue_tile(i + kAhead);
+    // slot 2i: A issues matrix work, B runs the softmax of the previous tile
+    if (grp == 0) mfma_phase(i);
+    else softmax_phase(i - 1);
     __syncthreads();
+    // slot 2i+1: A runs its softmax, B issues matrix work
+    if (grp == 0) softmax_phase(i);
+    else mfma_phase(i);
+    if (i < n_tiles) {
+      wait_next(i);
+      __syncthreads();
+    }
   }
 
   // ---- epilogue: O = u / l, LSE = (m + log2 l) * ln 2 ----
@@ -314,15 +411,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
 
 template <bool FP16, int D, bool CAUSAL>
 hipError_t launch_one(const FwdArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((fwd_kernel<FP16, D, CAUSAL>), dim3(a.grid), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((fwd_pingpong<FP16, D, CAUSAL>), dim3(a.grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
-}  // namespace
+}  // namespace pp
 
-int rows_per_workgroup() { return kBM; }
+int rows_per_workgroup() { return pp::kBM; }
 
 hipError_t launch_fwd(const FwdArgs& a, bool fp16, int d, bool causal, hipStream_t stream) {
+  using namespace pp;
   if (fp16) {
     if (d == 64) return causal ? launch_one<true, 64, true>(a, stream) : launch_one<true, 64, false>(a, stream);
     return causal ? launch_one<true, 128, true>(a, stream) : launch_one<true, 128, false>(a, stream);

@@ -56,7 +56,7 @@ typedef enum {
  *           log-sum-exp of each row's scaled scores.
  * B, H, N : batch, heads, sequence length (queries and keys share N). Any of them
  *           zero means there is nothing to do: FA_OK is returned and no pointer is
- *           touched. Requires N * d < 2^31 and B * H * ceil(N / 128) < 2^31.
+ *           touched. Requires N * d < 2^31 and B * H * ceil(N / 256) < 2^31.
  * d       : head dimension, 64 or 128.
  * causal  : 0 for full attention, 1 for causal (top-left aligned: query i sees
  *           keys 0..i).

@@ -63,8 +63,10 @@ def _oracle(qb, kb, vb, dtype, causal, scale, rows=None, heads=None):
     return oracle_attention(q, k, v, scale, causal=causal, rows=rows)
 
 
+# N spans one to three 256-row query tiles and up to 11 64-key tiles, with ragged ends
 SMALL_SHAPES = [(1, 1, 1, 64), (1, 1, 3, 128), (1, 2, 63, 64), (1, 1, 64, 128), (2, 3, 130, 64),
-                (1, 2, 200, 128), (1, 1, 257, 128), (2, 2, 384, 64), (1, 1, 511, 128)]
+                (1, 2, 200, 128), (1, 1, 257, 128), (2, 2, 384, 64), (1, 1, 511, 128), (1, 2, 700, 64),
+                (2, 1, 640, 128)]
 
 
 @pytest.mark.parametrize("causal", [False, True])
