@@ -70,14 +70,22 @@ constexpr int kStages = 4;        // LDS ring depth (tiles)
 constexpr int kAhead = kStages - 2;  // tiles in flight ahead of use
 constexpr uint32_t kBufferConfig = 0x00020000u;  // raw buffer descriptor word 3 (gfx9 family)
 
-// Reference-maximum slack in log2 units (see the header comment); 0 rescales
-// whenever a row maximum rises. 0 is the default: it keeps the dominant
-// probability of every row at exactly 2^0 = 1, which 16-bit P represents
-// exactly; with a slack the dominant term becomes 2^x, 0 < x <= TAU, and its
-// rounding to 16 bits reaches the output at about 2^-11 (fp16) of |O|.
-#ifndef FA_RESCALE_TAU
-#define FA_RESCALE_TAU 0
+// Reference-maximum slack in log2 units (see the header comment). With 0 the
+// accumulator is rescaled whenever a row maximum rises, and the dominant
+// probability of every row is exactly 2^0 = 1, which 16-bit P represents
+// exactly. With a slack the accumulator is rescaled only when a maximum rises by
+// more than the slack (rarely, after the first tiles), which saves the rescale's
+// VALU work; the dominant term then becomes 2^x, 0 < x <= TAU, rounded to 16 bits
+// like every other probability. bf16 outputs carry 8 bits, so the extra rounding
+// is below their resolution; fp16 keeps the exact running maximum.
+#ifndef FA_RESCALE_TAU_BF16
+#define FA_RESCALE_TAU_BF16 8
 #endif
+#ifndef FA_RESCALE_TAU_FP16
+#define FA_RESCALE_TAU_FP16 0
+#endif
+template <bool FP16>
+constexpr float kTau = FP16 ? (float)FA_RESCALE_TAU_FP16 : (float)FA_RESCALE_TAU_BF16;
 
 template <int D>
 struct Geo {
@@ -311,12 +319,16 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  // the matrix phase runs at raised issue priority so that, when both waves of a
+  // SIMD have an instruction ready, the matrix pipe is fed first
   auto mfma_phase = [&](int i) {
     const bool do_s = i < n_tiles && active(i);
     const bool do_p = i >= 1 && active(i - 1);
+    __builtin_amdgcn_s_setprio(1);
     if (do_s && do_p) mfma_steps(std::true_type{}, std::true_type{}, i);
     else if (do_s) mfma_steps(std::true_type{}, std::false_type{}, i);
     else if (do_p) mfma_steps(std::false_type{}, std::true_type{}, i);
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // online softmax of S(t): reference max, p, l, rescale of u, 16-bit P. Max and
@@ -346,7 +358,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
     }
     float mx = __builtin_fmaxf(__builtin_fmaxf(mc[0], mc[1]), __builtin_fmaxf(mc[2], mc[3]));
     mx = __builtin_fmaxf(mx, other_half(mx)) * sc;
-    const float m_new = (mx > m_run + (float)FA_RESCALE_TAU) ? mx : m_run;
+    const float m_new = (mx > m_run + kTau<FP16>) ? mx : m_run;
     const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
     float ps[4];
