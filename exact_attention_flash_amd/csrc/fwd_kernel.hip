@@ -18,18 +18,20 @@
 //    B operand of the P V product without leaving registers. V^T is read from the
 //    row-major V tile with ds_read_b64_tr_b16.
 //  * Ping-pong: waves 0-3 (group A) and 4-7 (group B) land on the four SIMDs in
-//    pairs. Every iteration has two barrier-separated slots; in each slot one
-//    group issues its matrix work (S of tile i and P V of tile i-1) while the other
-//    runs the softmax of its latest scores on the vector ALU, so MFMA and VALU work
-//    of the two waves sharing a SIMD overlap.
+//    pairs. In every iteration group A first issues its matrix work (S of tile i
+//    and P V of tile i-1) and then runs the softmax of tile i, while group B runs
+//    the softmax of tile i-1 first and then issues its matrix work, so the MFMA
+//    and VALU streams of the two waves sharing a SIMD overlap. One barrier per
+//    iteration publishes the next K/V tile.
 //  * K/V tiles are loaded straight into LDS with buffer_load ... lds (no staging
 //    registers) into a 4-stage ring, two tiles ahead of use. Rows past the end of
 //    the sequence read as zeros through the buffer descriptor's range. The tiles
 //    are stored unpadded with 16-byte chunks XOR-swizzled by row, chosen so that
 //    the K reads (16 lanes, 16 rows) and the transposing V reads (32 lanes, 4 rows)
 //    hit every LDS bank once.
-//  * Group A owns row blocks 0,2,4,6 and group B blocks 1,3,5,7, so under a causal
-//    mask both groups visit the same number of key tiles.
+//  * The pair of waves on SIMD k owns row blocks k and 7-k of the workgroup's eight
+//    blocks of 32 rows, so under a causal mask every SIMD has the same amount of
+//    work on the diagonal tiles and late diagonal tiles cost half an iteration.
 //  * Exponentials use exp2 with scale*log2(e) folded into one FMA per score.
 //  * Causal: tiles past the workgroup's last row are never loaded; waves skip the
 //    math of tiles entirely after their rows; only tiles on the diagonal or at the
@@ -37,11 +39,15 @@
 //  * Workgroup order: heaviest causal query tiles first; all query tiles of one
 //    (batch, head) on one XCD so K/V tiles are shared through its L2.
 //
-// Reference maximum: with TAU = 0 the reference is the running maximum. With TAU
-// > 0 (log2 units) a row keeps its reference until a tile's maximum exceeds it by
-// more than TAU; the rescaling identity of "6.1 FlashAttention V1 in detail", §3.3
-// holds for any reference, so u / l and m + ln l are unchanged, and exponent
-// arguments stay <= TAU (probabilities <= 2^TAU).
+// Reference maximum. The rescaling identity of "6.1 FlashAttention V1 in detail",
+// §3.3 holds for any per-row reference r: with p = 2^(s' - r) (s' the score in
+// log2 units), u / l and r + log2 l do not depend on r, as long as no p
+// overflows. fp16 keeps r equal to the running row maximum (p <= 1). bf16 keeps
+// the reference of the previous tile and skips the row maximum: the tile's
+// probabilities are computed against it directly, and only if there is no
+// reference yet (first tile) or some partial row sum exceeds 2^64 (an exponent
+// argument past 64) is the tile redone with the exact running maximum. bf16 P
+// carries 8 bits at any magnitude, so probabilities up to 2^64 lose nothing.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -70,22 +76,8 @@ constexpr int kStages = 4;        // LDS ring depth (tiles)
 constexpr int kAhead = kStages - 2;  // tiles in flight ahead of use
 constexpr uint32_t kBufferConfig = 0x00020000u;  // raw buffer descriptor word 3 (gfx9 family)
 
-// Reference-maximum slack in log2 units (see the header comment). With 0 the
-// accumulator is rescaled whenever a row maximum rises, and the dominant
-// probability of every row is exactly 2^0 = 1, which 16-bit P represents
-// exactly. With a slack the accumulator is rescaled only when a maximum rises by
-// more than the slack (rarely, after the first tiles), which saves the rescale's
-// VALU work; the dominant term then becomes 2^x, 0 < x <= TAU, rounded to 16 bits
-// like every other probability. bf16 outputs carry 8 bits, so the extra rounding
-// is below their resolution; fp16 keeps the exact running maximum.
-#ifndef FA_RESCALE_TAU_BF16
-#define FA_RESCALE_TAU_BF16 8
-#endif
-#ifndef FA_RESCALE_TAU_FP16
-#define FA_RESCALE_TAU_FP16 0
-#endif
-template <bool FP16>
-constexpr float kTau = FP16 ? (float)FA_RESCALE_TAU_FP16 : (float)FA_RESCALE_TAU_BF16;
+// partial row sums above this send a bf16 tile back through the exact maximum
+constexpr float kBig = 0x1p64f;
 
 template <int D>
 struct Geo {
@@ -194,8 +186,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
   const uint16_t* kg = reinterpret_cast<const uint16_t*>(a.k) + head_off;
   const uint16_t* vg = reinterpret_cast<const uint16_t*>(a.v) + head_off;
 
-  // rows of this wave: block 2*(wave%4) + grp of the workgroup's 8 blocks of 32
-  const int row0 = q0 + 32 * (2 * (wave & 3) + grp);
+  // rows of this wave: block wave%4 (group A) or 7 - wave%4 (group B) of the
+  // workgroup's 8 blocks of 32
+  const int row0 = q0 + 32 * (grp == 0 ? (wave & 3) : 7 - (wave & 3));
   const int qrow = row0 + l32;
 
   // ---- tiles visited by the workgroup ----
@@ -331,7 +324,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
     __builtin_amdgcn_s_setprio(0);
   };
 
-  // online softmax of S(t): reference max, p, l, rescale of u, 16-bit P. Max and
+  // online softmax of S(t): reference, p, l, rescale of u, 16-bit P. Maximum and
   // sum run as four independent chains to keep the VALU pipeline full.
   auto softmax_phase = [&](int t) {
     if (!(t >= 0 && t < n_tiles && active(t))) return;
@@ -347,33 +340,58 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[b][r] = (32 * b + 8 * (r >> 2) + (r & 3) > lim) ? -INFINITY : s[b][r];
     }
-    float mc[4];
+    // probabilities of this tile against the reference m_ref and their row sum
+    float pr[32];
+    auto exps = [&](float m_ref) {
+      float ps[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const f32x16& v = s[c >> 1];
-      const int o = 8 * (c & 1);
-      mc[c] = __builtin_fmaxf(__builtin_fmaxf(v[o], v[o + 1]), v[o + 2]);
+      for (int c = 0; c < 4; ++c) {
+        const f32x16& v = s[c >> 1];
+        const int o = 8 * (c & 1);
 #pragma unroll
-      for (int r = 3; r < 8; ++r) mc[c] = __builtin_fmaxf(mc[c], v[o + r]);
+        for (int r = 0; r < 8; ++r) pr[8 * c + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[o + r], sc, -m_ref));
+        const float* p = pr + 8 * c;
+        ps[c] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      }
+      return (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    };
+    // maximum of this lane's query over the tile (in-lane, then the other half-wave)
+    auto row_max = [&]() {
+      float mc[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const f32x16& v = s[c >> 1];
+        const int o = 8 * (c & 1);
+        mc[c] = __builtin_fmaxf(__builtin_fmaxf(v[o], v[o + 1]), v[o + 2]);
+#pragma unroll
+        for (int r = 3; r < 8; ++r) mc[c] = __builtin_fmaxf(mc[c], v[o + r]);
+      }
+      const float mx = __builtin_fmaxf(__builtin_fmaxf(mc[0], mc[1]), __builtin_fmaxf(mc[2], mc[3]));
+      return __builtin_fmaxf(mx, other_half(mx)) * sc;
+    };
+    float m_new = m_run, m_ref = m_run, lt = 0.f;
+    bool exact = true;
+    if constexpr (!FP16) {
+      exact = __any(m_run == -INFINITY);
+      if (!exact) {
+        lt = exps(m_run);
+        exact = __any(lt > kBig);
+      }
     }
-    float mx = __builtin_fmaxf(__builtin_fmaxf(mc[0], mc[1]), __builtin_fmaxf(mc[2], mc[3]));
-    mx = __builtin_fmaxf(mx, other_half(mx)) * sc;
-    const float m_new = (mx > m_run + kTau<FP16>) ? mx : m_run;
-    const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
-    float ps[4];
+    if (exact) {
+      const float mx = row_max();
+      m_new = (mx > m_run) ? mx : m_run;
+      m_ref = (m_new == -INFINITY) ? 0.f : m_new;
+      lt = exps(m_ref);
+    }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const f32x16& v = s[c >> 1];
-      const int o = 8 * (c & 1);
-      float p[8];
-#pragma unroll
-      for (int r = 0; r < 8; ++r) p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[o + r], sc, -m_ref));
-      ps[c] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      const float* p = pr + 8 * c;
       pb[c] = u32x4{pack2<FP16>(p[0], p[1]), pack2<FP16>(p[2], p[3]), pack2<FP16>(p[4], p[5]),
                     pack2<FP16>(p[6], p[7])};
     }
-    l_run = alpha * l_run + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
+    l_run = alpha * l_run + lt;
     m_run = m_new;
     if (__any(alpha != 1.0f)) {
 #pragma unroll
@@ -382,7 +400,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
   };
 
   // tile i+1 must have landed (every wave waits for its own loads) before the
-  // barrier that precedes slot 2(i+1); tile i+kAhead may stay in flight.
+  // barrier that ends iteration i; tile i+kAhead may stay in flight.
   auto wait_next = [&](int i) {
     if (i + kAhead < n_tiles) wait_vmcnt<G::loadsPerWave>();
     else wait_vmcnt<0>();
@@ -391,13 +409,15 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
   for (int i = 0; i <= n_tiles; ++i) {
     // refill the stage last used by tile i-2 with tile i+kAhead
     if (i + kAhead < n_tiles) issue_tile(i + kAhead);
-    // slot 2i: A issues matrix work, B runs the softmax of the previous tile
-    if (grp == 0) mfma_phase(i);
-    else softmax_phase(i - 1);
-    __syncthreads();
-    // slot 2i+1: A runs its softmax, B issues matrix work
-    if (grp == 0) softmax_phase(i);
-    else mfma_phase(i);
+    // A: matrix work of tile i, then its softmax; B: softmax of tile i-1, then
+    // matrix work of tile i
+    if (grp == 0) {
+      mfma_phase(i);
+      softmax_phase(i);
+    } else {
+      softmax_phase(i - 1);
+      mfma_phase(i);
+    }
     if (i < n_tiles) {
       wait_next(i);
       __syncthreads();

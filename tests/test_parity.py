@@ -212,3 +212,33 @@ def test_very_large_logits(fa, causal):
     # the scores reach ~1e4 in magnitude; the LSE bound is relative to them
     assert np.max(np.abs(lse - rl) / np.maximum(1.0, np.abs(rl))) <= 1e-6
     assert m["o_max_excess"] <= 1e-2 and m["o_mean_abs"] <= 1e-3
+
+
+@pytest.mark.parametrize("pattern", ["rising", "first_spike"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", [inputs.BF16, inputs.FP16])
+def test_reference_changes(fa, dtype, causal, pattern):
+    """Row maxima that move a long way between key tiles.
+
+    "rising": key tile j is scaled by 1 + j/2, so with scale 2 every tile's scores
+    exceed the previous tile's reference by far more than 2^64 in probability and the
+    reference must be replaced many times. "first_spike": key 0 is scaled by 8, so the
+    first tile's reference stays far above every later score and later
+    probabilities are tiny against it.
+    """
+    B, H, N, d = 1, 2, 700, 64
+    qb, kb, vb = inputs.draw_qkv((B, H, N, d), dtype, 1.0, 17)
+    k = inputs.bits_to_f64(kb, dtype)
+    if pattern == "rising":
+        k = k * (1.0 + 0.5 * (np.arange(N) // 64))[None, None, :, None]
+    else:
+        k[:, :, 0, :] *= 8.0
+    kb = inputs.to_bits(k.astype(np.float32), dtype)
+    scale = 2.0
+    o, lse = _run_gpu(fa, qb, kb, vb, dtype, causal, scale)
+    ro, rl = _oracle(qb, kb, vb, dtype, causal, scale)
+    m = metrics(o, lse, ro, rl, dtype)
+    _log(f"reference changes {pattern} {dtype} causal={causal}: {m}")
+    assert m["finite"]
+    assert np.max(np.abs(lse - rl) / np.maximum(1.0, np.abs(rl))) <= 1e-6
+    assert m["o_max_excess"] <= 1e-2 and m["o_mean_abs"] <= 1e-3
