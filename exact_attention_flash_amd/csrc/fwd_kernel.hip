@@ -10,7 +10,8 @@
 // the grid, key/value tiles stream through LDS, the accumulator stays in registers
 // and is divided once at the end.
 //
-// Workgroup: 8 wave64s, 256 query rows, 64-key tiles.
+// Persistent workgroups (one per compute unit) of 8 wave64s walk a list of work
+// items, each 256 query rows of one (batch, head); keys stream in 64-key tiles.
 //  * Each wave owns 32 query rows and computes S^T = K Q^T and O^T = V^T P^T with
 //    v_mfma_f32_32x32x16 (bf16 or fp16 in, fp32 out). In the 32x32 accumulator
 //    layout a lane holds one query and 16 keys, so row max and row sum are in-lane
@@ -24,11 +25,14 @@
 //    and VALU streams of the two waves sharing a SIMD overlap. One barrier per
 //    iteration publishes the next K/V tile.
 //  * K/V tiles are loaded straight into LDS with buffer_load ... lds (no staging
-//    registers) into a 4-stage ring, two tiles ahead of use. Rows past the end of
-//    the sequence read as zeros through the buffer descriptor's range. The tiles
-//    are stored unpadded with 16-byte chunks XOR-swizzled by row, chosen so that
-//    the K reads (16 lanes, 16 rows) and the transposing V reads (32 lanes, 4 rows)
-//    hit every LDS bank once.
+//    registers) into a 3-stage ring, one tile ahead of use; the tile stream runs
+//    across work items, so the next item's first tile is in flight while the
+//    current item finishes. Q rows of an item take the same path into a fourth
+//    LDS region one item ahead (160 KiB of LDS in all). Rows past the end of the
+//    sequence read as zeros through the buffer descriptor's range. Tiles are
+//    stored unpadded with 16-byte chunks XOR-swizzled by row, chosen so that the
+//    K and Q reads (16 lanes, 16 rows) and the transposing V reads (32 lanes, 4
+//    rows) hit every LDS bank once.
 //  * The pair of waves on SIMD k owns row blocks k and 7-k of the workgroup's eight
 //    blocks of 32 rows, so under a causal mask every SIMD has the same amount of
 //    work on the diagonal tiles and late diagonal tiles cost half an iteration.
@@ -36,8 +40,9 @@
 //  * Causal: tiles past the workgroup's last row are never loaded; waves skip the
 //    math of tiles entirely after their rows; only tiles on the diagonal or at the
 //    end of the sequence evaluate the mask.
-//  * Workgroup order: heaviest causal query tiles first; all query tiles of one
-//    (batch, head) on one XCD so K/V tiles are shared through its L2.
+//  * Item order: heaviest causal query tiles first, dealt to the workgroups in
+//    snake order so that every workgroup gets the same causal work; all query
+//    tiles of one (batch, head) on one XCD so K/V tiles are shared through its L2.
 //
 // Reference maximum. The rescaling identity of "6.1 FlashAttention V1 in detail",
 // §3.3 holds for any per-row reference r: with p = 2^(s' - r) (s' the score in
@@ -51,6 +56,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "fwd_kernel.h"
@@ -72,7 +78,7 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;  // query rows per workgroup
 constexpr int kBN = 64;           // keys per tile
-constexpr int kStages = 4;        // LDS ring depth (tiles)
+constexpr int kStages = 3;        // LDS ring depth (tiles)
 constexpr int kAhead = kStages - 2;  // tiles in flight ahead of use
 constexpr uint32_t kBufferConfig = 0x00020000u;  // raw buffer descriptor word 3 (gfx9 family)
 
@@ -85,8 +91,10 @@ struct Geo {
   static constexpr int chunksPerRow = D / 8;  // 16-byte chunks
   static constexpr int tileBytes = kBN * rowBytes;
   static constexpr int stageBytes = 2 * tileBytes;  // K then V
+  static constexpr int qBytes = kBM * rowBytes;       // the Q rows of one item
   static constexpr int blocksPerTile = tileBytes / 1024;  // 1 KiB per wave-instruction
   static constexpr int loadsPerWave = 2 * blocksPerTile / kWaves;  // K + V instructions per wave per tile
+  static constexpr int qLoadsPerWave = qBytes / 1024 / kWaves;       // Q instructions per wave per item
   static_assert(blocksPerTile % kWaves == 0, "tile must split into whole 1 KiB blocks per wave");
   // XOR swizzle of the 16-byte chunk index within a row
   __device__ static __forceinline__ int swz(int row) {
@@ -155,7 +163,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 template <bool FP16, int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
   using G = Geo<D>;
-  __shared__ __attribute__((aligned(1024))) char smem[kStages * G::stageBytes];
+  __shared__ __attribute__((aligned(1024))) char smem[kStages * G::stageBytes + G::qBytes];
+  char* const qsm = smem + kStages * G::stageBytes;  // Q rows of the current item
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -164,37 +173,43 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
-  // ---- workgroup -> (batch*head, query tile) ----
+  // ---- persistent schedule ----
+  // Work items are (slice, query tile) pairs, ranked heaviest causal query tile
+  // first. With xcd_grouped, the workgroups of XCD x (blockIdx % 8 == x) own slices
+  // [x*hpx, (x+1)*hpx), so all query tiles of a slice share K/V through one L2.
+  // Workgroup k of a group of size G takes the items k, 2G-1-k, 2G+k, 4G-1-k, ...
+  // of its group's ranked list (snake order), which gives every workgroup the same
+  // causal work when the list is a whole number of rounds.
   const int bid = blockIdx.x;
-  const int bh_count = a.bh;
-  int bh, rank;
+  int wg_k, wg_n, hpx, bh_base;
   if (a.xcd_grouped) {
-    const int hpx = bh_count / 8;
-    const int xcd = bid & 7, t = bid >> 3;
-    rank = t / hpx;
-    bh = xcd * hpx + t % hpx;
+    hpx = a.bh >> 3;
+    wg_k = bid >> 3;
+    wg_n = (int)gridDim.x >> 3;
+    bh_base = (bid & 7) * hpx;
   } else {
-    rank = bid / bh_count;
-    bh = bid % bh_count;
+    hpx = a.bh;
+    wg_k = bid;
+    wg_n = (int)gridDim.x;
+    bh_base = 0;
   }
-  const int qtile = CAUSAL ? (a.q_tiles - 1 - rank) : rank;
+  const int n_items = hpx * a.q_tiles;
   const int N = a.n;
-  const int q0 = qtile * kBM;
-  const int64_t head_off = (int64_t)bh * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const uint16_t* qg = reinterpret_cast<const uint16_t*>(a.q) + head_off;
-  const uint16_t* kg = reinterpret_cast<const uint16_t*>(a.k) + head_off;
-  const uint16_t* vg = reinterpret_cast<const uint16_t*>(a.v) + head_off;
-
-  // rows of this wave: block wave%4 (group A) or 7 - wave%4 (group B) of the
-  // workgroup's 8 blocks of 32
-  const int row0 = q0 + 32 * (grp == 0 ? (wave & 3) : 7 - (wave & 3));
-  const int qrow = row0 + l32;
-
-  // ---- tiles visited by the workgroup ----
   const int tiles_all = (N + kBN - 1) / kBN;
-  int n_tiles = tiles_all;
-  if (CAUSAL) n_tiles = min(tiles_all, (min(q0 + kBM, N) - 1) / kBN + 1);
+  // r-th item of this workgroup, or -1 past the end of its list
+  auto item_index = [&](int r) {
+    const int j = r * wg_n + ((r & 1) ? wg_n - 1 - wg_k : wg_k);
+    return j < n_items ? j : -1;
+  };
+  auto item_bh = [&](int j) { return bh_base + j % hpx; };
+  auto item_q0 = [&](int j) { return (CAUSAL ? (a.q_tiles - 1 - j / hpx) : j / hpx) * kBM; };
+  // key tiles visited by a query tile starting at q0 (causal: up to its last row)
+  auto item_tiles = [&](int q0) {
+    return CAUSAL ? min(tiles_all, (min(q0 + kBM, N) - 1) / kBN + 1) : tiles_all;
+  };
+  // this wave's block of 32 rows: block wave%4 (group A) or 7 - wave%4 (group B)
+  const int wave_rows = 32 * (grp == 0 ? (wave & 3) : 7 - (wave & 3));
 
   // ---- direct-to-LDS tile loads: this wave fills blocks wave + 8*i of K and of V ----
   // lane `lane` of block b lands at chunk position 64*b + lane = (row, physical chunk);
@@ -206,31 +221,77 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
     const int row = p / G::chunksPerRow, phys = p % G::chunksPerRow;
     ld_off[i] = (uint32_t)row * G::rowBytes + (uint32_t)((phys ^ G::swz(row)) * 16);
   }
-  auto issue_tile = [&](int t) {
-    const uint32_t skip = (uint32_t)t * kBN * G::rowBytes;
-    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(kg + (int64_t)t * kBN * D, head_bytes - skip);
-    const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(vg + (int64_t)t * kBN * D, head_bytes - skip);
-    char* st = smem + (t % kStages) * G::stageBytes;
+  // The workgroup's key tiles form one stream over its items; tile g of the stream
+  // lives in ring stage g % kStages. A cursor walks the stream kAhead tiles ahead
+  // of the matrix work, so the first tiles of the next item are in flight while the
+  // current item finishes.
+  int c_r = 0, c_j = item_index(0), c_t = 0, c_n = 0, c_g = 0;
+  const uint16_t *c_k = nullptr, *c_v = nullptr;
+  auto cursor_item = [&]() {
+    if (c_j < 0) return;
+    const int64_t off = (int64_t)item_bh(c_j) * N * D;
+    c_k = reinterpret_cast<const uint16_t*>(a.k) + off;
+    c_v = reinterpret_cast<const uint16_t*>(a.v) + off;
+    c_n = item_tiles(item_q0(c_j));
+    c_t = 0;
+  };
+  cursor_item();
+  // issue the cursor's tile and advance; false once the stream is exhausted
+  auto issue_next = [&]() {
+    if (c_j < 0) return false;
+    const uint32_t skip = (uint32_t)c_t * kBN * G::rowBytes;
+    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(c_k + (int64_t)c_t * kBN * D, head_bytes - skip);
+    const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(c_v + (int64_t)c_t * kBN * D, head_bytes - skip);
+    char* st = smem + (c_g % kStages) * G::stageBytes;
 #pragma unroll
     for (int i = 0; i < G::blocksPerTile / kWaves; ++i) {
       buffer_load16_lds(kr, ld_off[i], st + 1024 * (wave + kWaves * i));
       buffer_load16_lds(vr, ld_off[i], st + G::tileBytes + 1024 * (wave + kWaves * i));
     }
+    ++c_g;
+    if (++c_t == c_n) {
+      c_j = item_index(++c_r);
+      cursor_item();
+    }
+    return true;
+  };
+  if (c_j < 0) return;  // no work for this workgroup
+
+  // Q rows of an item go to LDS like K tiles (same chunk swizzle, 256 rows); at the
+  // start of the item every lane reads its query's row into the B operands
+  // (k-slots d = 16*kk + 8*h + 0..7), and once every wave has done so the next
+  // item's Q is loaded while this item runs.
+  auto issue_q = [&](int j) {
+    const int q0 = item_q0(j);
+    const __amdgpu_buffer_rsrc_t qr =
+        buffer_rsrc(reinterpret_cast<const uint16_t*>(a.q) + (int64_t)item_bh(j) * N * D + (int64_t)q0 * D,
+                    head_bytes - (uint32_t)q0 * G::rowBytes);
+    int lw = lane + 64 * wave;
+    asm volatile("" : "+v"(lw));  // recomputed per call rather than kept live
+#pragma unroll
+    for (int i = 0; i < G::qLoadsPerWave; ++i) {
+      const int p = lw + 64 * kWaves * i;
+      const int row = p / G::chunksPerRow, phys = p % G::chunksPerRow;
+      buffer_load16_lds(qr, (uint32_t)row * G::rowBytes + (uint32_t)((phys ^ G::swz(row)) * 16),
+                        qsm + 1024 * (wave + kWaves * i));
+    }
+  };
+  u32x4 qreg[D / 16];
+  auto read_q = [&]() {
+    int row = wave_rows + l32;
+    asm volatile("" : "+v"(row));  // recomputed per call rather than kept live
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+      qreg[kk] = lds_read16(qsm + row * G::rowBytes + (((2 * kk + h) ^ G::swz(row)) * 16));
   };
 
-  // prologue: the first kAhead tiles go in flight, then the Q rows of this lane's
-  // query (B operands, k-slots d = 16*kk + 8*h + 0..7); one wait covers all of them,
-  // so the compiler also sees the Q registers complete before the loop.
-  issue_tile(0);
-  if (n_tiles > 1) issue_tile(1);
-  u32x4 qreg[D / 16];
-  {
-    const __amdgpu_buffer_rsrc_t qr = buffer_rsrc(qg, head_bytes);
+  // prologue: the first item's Q and the first kAhead tiles of the stream (the
+  // cursor may move past the first item while doing so)
+  const int first_j = c_j;
+  issue_q(first_j);
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) qreg[kk] = buffer_load16(qr, (uint32_t)qrow * G::rowBytes + kk * 32 + h * 16);
-  }
-  wait_vmcnt<0>();
-  __syncthreads();
+  for (int t = 0; t < kAhead; ++t) issue_next();
+  bool first = true;
 
   // ---- per-lane LDS offsets (within a stage) ----
   // K: row l32 (+32 for the second block of keys), logical chunk 2*kk + h
@@ -251,16 +312,17 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
     }
 
   const float sc = a.scale_log2;
-  float m_run = -INFINITY;  // reference maximum (log2 units) of this lane's query
-  float l_run = 0.f;        // denominator over this half-wave's keys
+  float m_run;  // reference maximum (log2 units) of this lane's query
+  float l_run;  // denominator over this half-wave's keys
   f32x16 acc[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
   f32x16 s[2] = {f32x16{}, f32x16{}};
   u32x4 pb[4] = {u32x4{}, u32x4{}, u32x4{}, u32x4{}};
 
-  const int wave_last_row = row0 + 31;
-  auto active = [&](int t) { return row0 < N && (!CAUSAL || t * kBN <= wave_last_row); };
+  // the current item: its first row, this wave's rows, its key tiles and the
+  // stream index of its tile 0
+  int it_r = 0, it_j = first_j;
+  int row0 = 0, qrow = 0, n_tiles = 0, g0 = 0;
+  auto active = [&](int t) { return row0 < N && (!CAUSAL || t * kBN <= row0 + 31); };
 
   // per-lane K offsets: row l32 (the second block of 32 keys adds 32 rows), logical
   // chunk 2*kk + h
@@ -281,8 +343,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
   auto mfma_steps = [&](auto do_s_c, auto do_p_c, int i) {
     constexpr bool DO_S = decltype(do_s_c)::value;
     constexpr bool DO_P = decltype(do_p_c)::value;
-    const char* kt = smem + (i % kStages) * G::stageBytes;
-    const char* vt = smem + ((i + kStages - 1) % kStages) * G::stageBytes + G::tileBytes;
+    const char* kt = smem + ((g0 + i) % kStages) * G::stageBytes;
+    const char* vt = smem + ((g0 + i + kStages - 1) % kStages) * G::stageBytes + G::tileBytes;
     u32x4 kop[kLook + 1];
     u32x2 vlo[kLook + 1], vhi[kLook + 1];
     auto issue = [&](int st) {
@@ -399,45 +461,76 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
     }
   };
 
-  // tile i+1 must have landed (every wave waits for its own loads) before the
-  // barrier that ends iteration i; tile i+kAhead may stay in flight.
-  auto wait_next = [&](int i) {
-    if (i + kAhead < n_tiles) wait_vmcnt<G::loadsPerWave>();
-    else wait_vmcnt<0>();
-  };
-
-  for (int i = 0; i <= n_tiles; ++i) {
-    // refill the stage last used by tile i-2 with tile i+kAhead
-    if (i + kAhead < n_tiles) issue_tile(i + kAhead);
-    // A: matrix work of tile i, then its softmax; B: softmax of tile i-1, then
-    // matrix work of tile i
-    if (grp == 0) {
-      mfma_phase(i);
-      softmax_phase(i);
-    } else {
-      softmax_phase(i - 1);
-      mfma_phase(i);
-    }
-    if (i < n_tiles) {
-      wait_next(i);
-      __syncthreads();
-    }
-  }
-
-  // ---- epilogue: O = u / l, LSE = (m + log2 l) * ln 2 ----
-  const float l_tot = l_run + other_half(l_run);
-  if (qrow < N) {
-    const float inv = 1.0f / l_tot;
-    uint16_t* og = reinterpret_cast<uint16_t*>(a.o) + head_off + (int64_t)qrow * D;
+  for (;;) {
+    // the item's Q and first tile were issued during the previous item and waited
+    // for before its epilogue (for the first item: in the prologue), so the
+    // previous item's stores may still be in flight here
+    if (first) wait_vmcnt<0>();
+    first = false;
+    __syncthreads();
+    read_q();
+    const int bh = item_bh(it_j);
+    row0 = item_q0(it_j) + wave_rows;
+    qrow = row0 + l32;
+    n_tiles = item_tiles(item_q0(it_j));
+    const int next_j = item_index(it_r + 1);
+    m_run = -INFINITY;
+    l_run = 0.f;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const u32x2 w = {pack2<FP16>(acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv),
-                         pack2<FP16>(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv)};
-        *reinterpret_cast<u32x2*>(og + db * 32 + 8 * g + 4 * h) = w;
+    for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
+
+    // once every wave holds its Q rows (this barrier), the next item's Q may be
+    // loaded; it is issued after the first tile load so that the wait for that tile
+    // can leave it in flight for another iteration
+    __syncthreads();
+    for (int i = 0; i <= n_tiles; ++i) {
+      // one stream tile per iteration keeps the cursor kAhead tiles ahead; its stage
+      // last held the tile kStages - kAhead before it, read before the last barrier
+      bool issued = false;
+      if (i < n_tiles) issued = issue_next();
+      const bool q_in_flight = i == 0 && next_j >= 0;
+      if (q_in_flight) issue_q(next_j);
+      // A: matrix work of tile i, then its softmax; B: softmax of tile i-1, then
+      // matrix work of tile i
+      if (grp == 0) {
+        mfma_phase(i);
+        softmax_phase(i);
+      } else {
+        softmax_phase(i - 1);
+        mfma_phase(i);
       }
-    if (h == 0) a.lse[(int64_t)bh * N + qrow] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994530942f;
+      // tile i+1 must have landed (every wave waits for its own loads) before the
+      // barrier that publishes it; only the next item's Q may still be in flight
+      if (i + 1 < n_tiles) {
+        if (q_in_flight) wait_vmcnt<G::qLoadsPerWave>();
+        else wait_vmcnt<0>();
+        __syncthreads();
+      }
+      (void)issued;
+    }
+
+    // ---- epilogue: O = u / l, LSE = (m + log2 l) * ln 2 ----
+    // the next item's Q and first tile are the only loads in flight: wait for them
+    // here, before the stores, so that the next item need not wait for the stores
+    wait_vmcnt<0>();
+    const float l_tot = l_run + other_half(l_run);
+    if (qrow < N) {
+      const float inv = 1.0f / l_tot;
+      uint16_t* og = reinterpret_cast<uint16_t*>(a.o) + (int64_t)bh * N * D + (int64_t)qrow * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const u32x2 w = {pack2<FP16>(acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv),
+                           pack2<FP16>(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv)};
+          *reinterpret_cast<u32x2*>(og + db * 32 + 8 * g + 4 * h) = w;
+        }
+      if (h == 0) a.lse[(int64_t)bh * N + qrow] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994530942f;
+    }
+    if (next_j < 0) break;
+    g0 += n_tiles;
+    it_j = next_j;
+    ++it_r;
   }
 }
 
@@ -447,12 +540,40 @@ hipError_t launch_one(const FwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// compute units of the current device, queried once per device
+int device_cus() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64) cached[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
 }  // namespace pp
 
 int rows_per_workgroup() { return pp::kBM; }
 
-hipError_t launch_fwd(const FwdArgs& a, bool fp16, int d, bool causal, hipStream_t stream) {
+hipError_t launch_fwd(const FwdArgs& args, bool fp16, int d, bool causal, hipStream_t stream) {
   using namespace pp;
+  // persistent grid: one workgroup per compute unit (the LDS ring admits one per
+  // CU), never more than there are items; a multiple of 8 when slices are grouped
+  // by XCD so that every XCD gets the same number of workgroups
+  FwdArgs a = args;
+  const int cus = device_cus();
+  if (cus <= 0) return hipErrorInvalidDevice;
+  int grid = a.bh * a.q_tiles;
+  if (grid > cus) grid = cus;
+  if (a.xcd_grouped) {
+    grid &= ~7;
+    if (grid < 8) grid = 8;
+  }
+  a.grid = grid;
   if (fp16) {
     if (d == 64) return causal ? launch_one<true, 64, true>(a, stream) : launch_one<true, 64, false>(a, stream);
     return causal ? launch_one<true, 128, true>(a, stream) : launch_one<true, 128, false>(a, stream);
