@@ -1,4 +1,4 @@
-"""MI355X-native exact attention forward (FlashAttention-style), bf16/fp16.
+"""MI355X-native exact attention forward and backward (FlashAttention-style), bf16/fp16.
 
 The computation runs entirely in the gfx950 HIP kernels behind the C ABI of
 include/flash_attn.h; this module only checks and marshals torch tensors
@@ -13,13 +13,13 @@ from . import _native
 from ._native import (FA_BF16, FA_FP16, FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEADDIM,  # noqa: F401
                       FA_ERR_DTYPE, FA_ERR_SCALE, FA_ERR_ALIGN, FA_ERR_ALIAS, FA_ERR_HIP, FA_ERR_ARG)
 
-__all__ = ["forward", "flash_attn_fwd", "flash_attn_strerror", "flash_attn_abi_version"]
+__all__ = ["forward", "backward", "flash_attn_fwd", "flash_attn_bwd", "flash_attn_strerror", "flash_attn_abi_version"]
 
 
 class FlashAttnError(RuntimeError):
-    def __init__(self, status: int):
+    def __init__(self, status: int, call: str = "flash_attn_fwd"):
         self.status = status
-        super().__init__(f"flash_attn_fwd failed ({status}): {_native.strerror(status)}")
+        super().__init__(f"{call} failed ({status}): {_native.strerror(status)}")
 
 
 def _dtype_code(t):
@@ -76,6 +76,59 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, stream=No
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     flash_attn_fwd(q, k, v, o, lse, causal=causal, scale=scale, stream=stream)
     return o, lse
+
+
+def flash_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, causal: bool = False, scale: float | None = None,
+                   stream=None) -> None:
+    """Run the backward kernels on caller-owned tensors (the C entry point with torch arguments).
+
+    q, k, v, o, dout, dq, dk, dv: contiguous [B, H, N, d] CUDA tensors of q's dtype;
+    lse (the forward's) and delta (workspace): contiguous [B, H, N] float32.
+    Asynchronous on ``stream`` (default: the current stream).
+    """
+    import torch
+
+    if q.dim() != 4:
+        raise ValueError("q must have shape [B, H, N, d]")
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{name} must match q in shape and dtype")
+    B, H, N, d = q.shape
+    for name, t in (("lse", lse), ("delta", delta)):
+        if t.shape != (B, H, N) or t.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32 with shape [B, H, N]")
+    tensors = (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("lse", lse), ("dq", dq), ("dk", dk),
+               ("dv", dv), ("delta", delta))
+    for name, t in tensors:
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.device != q.device:
+            raise ValueError("all tensors must be on one device")
+    dtype = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = _native.bwd_raw(*(t.data_ptr() for _, t in tensors), B, H, N, d, causal, scale, stream.cuda_stream, dtype)
+    if st != FA_OK:
+        raise FlashAttnError(st, "flash_attn_bwd")
+
+
+def backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None, stream=None):
+    """Allocate dq, dk, dv (q's dtype) and the delta workspace and run the backward pass.
+
+    o and lse are the forward's outputs for the same q, k, v, causal and scale.
+    Returns (dq, dk, dv).
+    """
+    import torch
+
+    B, H, N, _ = q.shape
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    flash_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, causal=causal, scale=scale, stream=stream)
+    return dq, dk, dv
 
 
 def flash_attn_strerror(status: int) -> str:

@@ -40,6 +40,13 @@ def lib() -> ctypes.CDLL:
         ]
         L.flash_attn_fwd_validate.restype = ctypes.c_int
         L.flash_attn_fwd_validate.argtypes = L.flash_attn_fwd.argtypes
+        L.flash_attn_bwd.restype = ctypes.c_int
+        L.flash_attn_bwd.argtypes = [ctypes.c_void_p] * 10 + [
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_int,
+        ]
+        L.flash_attn_bwd_validate.restype = ctypes.c_int
+        L.flash_attn_bwd_validate.argtypes = L.flash_attn_bwd.argtypes
         L.flash_attn_strerror.restype = ctypes.c_char_p
         L.flash_attn_strerror.argtypes = [ctypes.c_int]
         L.flash_attn_abi_version.restype = ctypes.c_int
@@ -56,6 +63,18 @@ def fwd_raw(q, k, v, o, lse, B, H, N, d, causal, scale, stream, dtype) -> int:
 def validate_raw(q, k, v, o, lse, B, H, N, d, causal, scale, stream, dtype) -> int:
     """Call flash_attn_fwd_validate (host checks only, never launches)."""
     return lib().flash_attn_fwd_validate(q, k, v, o, lse, B, H, N, d, int(causal), float(scale), stream, dtype)
+
+
+def bwd_raw(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, causal, scale, stream, dtype) -> int:
+    """Call flash_attn_bwd with integer addresses; returns the status code."""
+    return lib().flash_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, int(causal), float(scale),
+                                stream, dtype)
+
+
+def validate_bwd_raw(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, causal, scale, stream, dtype) -> int:
+    """Call flash_attn_bwd_validate (host checks only, never launches)."""
+    return lib().flash_attn_bwd_validate(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, int(causal),
+                                         float(scale), stream, dtype)
 
 
 def strerror(status: int) -> str:

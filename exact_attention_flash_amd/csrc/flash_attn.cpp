@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdint>
 
+#include "bwd_kernel.h"
 #include "fwd_kernel.h"
 
 namespace {
@@ -21,7 +22,7 @@ bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p
 
 }  // namespace
 
-extern "C" int flash_attn_abi_version(void) { return 1; }
+extern "C" int flash_attn_abi_version(void) { return 2; }
 
 extern "C" const char* flash_attn_strerror(int status) {
   switch (status) {
@@ -31,8 +32,8 @@ extern "C" const char* flash_attn_strerror(int status) {
     case FA_ERR_HEADDIM: return "head dimension d must be 64 or 128";
     case FA_ERR_DTYPE: return "dtype must be FA_BF16 or FA_FP16";
     case FA_ERR_SCALE: return "scale must be finite and > 0";
-    case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
-    case FA_ERR_ALIAS: return "o or lse overlaps an input, or o overlaps lse";
+    case FA_ERR_ALIGN: return "16-bit tensors must be 16-byte aligned and fp32 ones 4-byte aligned";
+    case FA_ERR_ALIAS: return "an output overlaps an input or another output";
     case FA_ERR_HIP: return "HIP runtime error at launch";
     case FA_ERR_ARG: return "causal must be 0 or 1";
     default: return "unknown status";
@@ -107,6 +108,88 @@ extern "C" int flash_attn_fwd(const void* q, const void* k, const void* v, void*
   const int st = check_args(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, &a, &empty);
   if (st != FA_OK || empty) return st;
   const hipError_t err = fa::launch_fwd(a, dtype == FA_FP16, static_cast<int>(d), causal == 1,
+                                        static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+namespace {
+
+// All host-side checks of the backward call; on success fills the launch arguments.
+int check_bwd_args(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                   void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t H, int64_t N, int64_t d,
+                   int causal, float scale, int dtype, fa::BwdArgs* a, bool* empty) {
+  *empty = false;
+  if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (dtype != FA_BF16 && dtype != FA_FP16) return FA_ERR_DTYPE;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
+  if (B == 0 || H == 0 || N == 0) {
+    *empty = true;
+    return FA_OK;
+  }
+  // a slice is addressed with 32-bit offsets; grids of bh * ceil(N / 128) workgroups
+  if (N * d > INT32_MAX - 1) return FA_ERR_SHAPE;
+  if (B > INT32_MAX / H) return FA_ERR_SHAPE;
+  const int64_t bh = B * H;
+  if (bh > INT32_MAX / ((N + 127) / 128)) return FA_ERR_SHAPE;
+  if (bh * N > INT32_MAX / 4) return FA_ERR_SHAPE;
+
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !delta) return FA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4) || !aligned(delta, 4))
+    return FA_ERR_ALIGN;
+  const uint64_t t = static_cast<uint64_t>(bh) * N * d * 2;  // one 16-bit tensor
+  const uint64_t r = static_cast<uint64_t>(bh) * N * 4;      // one fp32 row statistic
+  const void* ins[] = {q, k, v, o, dout, lse};
+  const uint64_t in_n[] = {t, t, t, t, t, r};
+  const void* outs[] = {dq, dk, dv, delta};
+  const uint64_t out_n[] = {t, t, t, r};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outs[i], out_n[i], ins[j], in_n[j])) return FA_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], out_n[i], outs[j], out_n[j])) return FA_ERR_ALIAS;
+  }
+
+  a->q = q;
+  a->k = k;
+  a->v = v;
+  a->o = o;
+  a->dout = dout;
+  a->lse = lse;
+  a->dq = dq;
+  a->dk = dk;
+  a->dv = dv;
+  a->delta = delta;
+  a->bh = static_cast<int>(bh);
+  a->n = static_cast<int>(N);
+  a->xcd_grouped = (bh % 8 == 0) ? 1 : 0;
+  a->scale = scale;
+  a->scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634074);
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" int flash_attn_bwd_validate(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                       const float* lse, void* dq, void* dk, void* dv, float* delta, int64_t B,
+                                       int64_t H, int64_t N, int64_t d, int causal, float scale, void* /*stream*/,
+                                       int dtype) {
+  fa::BwdArgs a;
+  bool empty;
+  return check_bwd_args(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, causal, scale, dtype, &a, &empty);
+}
+
+extern "C" int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                              const float* lse, void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t H,
+                              int64_t N, int64_t d, int causal, float scale, void* stream, int dtype) {
+  fa::BwdArgs a;
+  bool empty;
+  const int st =
+      check_bwd_args(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, causal, scale, dtype, &a, &empty);
+  if (st != FA_OK || empty) return st;
+  const hipError_t err = fa::launch_bwd(a, dtype == FA_FP16, static_cast<int>(d), causal == 1,
                                         static_cast<hipStream_t>(stream));
   return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

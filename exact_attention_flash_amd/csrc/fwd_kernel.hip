@@ -60,19 +60,12 @@
 #include <type_traits>
 
 #include "fwd_kernel.h"
+#include "gfx950_ops.h"
 
 namespace fa {
 namespace pp {
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+using namespace ::fa::ops;
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
@@ -80,7 +73,6 @@ constexpr int kBM = 32 * kWaves;  // query rows per workgroup
 constexpr int kBN = 64;           // keys per tile
 constexpr int kStages = 3;        // LDS ring depth (tiles)
 constexpr int kAhead = kStages - 2;  // tiles in flight ahead of use
-constexpr uint32_t kBufferConfig = 0x00020000u;  // raw buffer descriptor word 3 (gfx9 family)
 
 // partial row sums above this send a bf16 tile back through the exact maximum
 constexpr float kBig = 0x1p64f;
@@ -96,69 +88,8 @@ struct Geo {
   static constexpr int loadsPerWave = 2 * blocksPerTile / kWaves;  // K + V instructions per wave per tile
   static constexpr int qLoadsPerWave = qBytes / 1024 / kWaves;       // Q instructions per wave per item
   static_assert(blocksPerTile % kWaves == 0, "tile must split into whole 1 KiB blocks per wave");
-  // XOR swizzle of the 16-byte chunk index within a row
-  __device__ static __forceinline__ int swz(int row) {
-    if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
-    else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
-  }
+  __device__ static __forceinline__ int swz(int row) { return chunk_swizzle<D>(row); }
 };
-
-template <bool FP16>
-__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
-  if constexpr (FP16) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
-                                                  0, 0, 0);
-  } else {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
-                                                   0, 0, 0);
-  }
-}
-
-template <bool FP16>
-__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  const f32x2 v = {lo, hi};
-  if constexpr (FP16) return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
-  else return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
-
-__device__ __forceinline__ float other_half(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return (threadIdx.x & 32) ? __uint_as_float(r[0]) : __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
-  s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
-  return __builtin_bit_cast(u32x2, r);
-}
-
-__device__ __forceinline__ u32x4 lds_read16(const char* p) { return *reinterpret_cast<const u32x4*>(p); }
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kBufferConfig);
-}
-
-__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
-}
-
-// 16 bytes per lane from the buffer straight into LDS at lds_base + 16 * lane
-// (buffer_load_dwordx4 ... lds; M0 holds the wave-uniform LDS base). Written as
-// inline assembly so that the compiler does not treat every later LDS read as
-// possibly aliasing the in-flight copy (it would then wait for all outstanding
-// loads, tiles prefetched for later iterations included); completion is instead
-// awaited explicitly with wait_vmcnt before the barrier that publishes a tile.
-__device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, uint32_t off, char* lds_base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)lds_base));
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(m0) : "memory");
-}
-
-// s_waitcnt on the vector-memory counter only (gfx9 encoding: expcnt and lgkmcnt at max).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
 
 template <bool FP16, int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {

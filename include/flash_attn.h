@@ -1,5 +1,6 @@
 /*
- * flash_attn.h -- C ABI of the MI355X (gfx950) exact attention forward pass.
+ * flash_attn.h -- C ABI of the MI355X (gfx950) exact attention forward and
+ * backward passes.
  *
  * The operation: for every batch b, head h and query row i,
  *
@@ -39,8 +40,8 @@ typedef enum {
   FA_ERR_HEADDIM = -3, /* d is not 64 or 128                                      */
   FA_ERR_DTYPE = -4,   /* dtype is neither FA_BF16 nor FA_FP16                    */
   FA_ERR_SCALE = -5,   /* scale is not finite or not > 0                          */
-  FA_ERR_ALIGN = -6,   /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
-  FA_ERR_ALIAS = -7,   /* o or lse overlaps an input, or o overlaps lse          */
+  FA_ERR_ALIGN = -6,   /* a 16-bit tensor not 16-byte aligned, or an fp32 one not 4-byte aligned */
+  FA_ERR_ALIAS = -7,   /* an output overlaps an input or another output          */
   FA_ERR_HIP = -8,     /* the HIP runtime reported an error at launch             */
   FA_ERR_ARG = -9      /* causal is not 0 or 1                                    */
 } fa_status;
@@ -89,10 +90,58 @@ int flash_attn_fwd_validate(const void* q, const void* k, const void* v, void* o
                             int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
                             void* stream, int dtype);
 
+/*
+ * flash_attn_bwd -- gradients of the forward pass with respect to q, k and v.
+ *
+ * For the loss gradient dout = dL/do of o = flash_attn_fwd(q, k, v), with
+ * S = scale * q k^T (masked like the forward) and P = softmax(S) row by row:
+ *
+ *     dv = P^T dout,  dP = dout v^T,  dS = P o (dP - D),  dq = scale * dS k,
+ *     dk = scale * dS^T q,   D_i = rowsum(dout o o)_i   ("o" elementwise)
+ *
+ * ("6.1 FlashAttention V1 in detail", §6.1 and §6.2; "FlashAttention: IO-Aware
+ * Tiling, Online Softmax Mathematics, Memory Hierarchy Dynamics, and Kernel
+ * Evolution", section "Backward Pass Recomputation", where scale = 1/sqrt(d)).
+ * P is rebuilt tile by tile from q, k and lse (P = exp(S - lse)); no N x N
+ * matrix is ever written to memory.
+ *
+ * q, k, v : device, contiguous [B, H, N, d] of `dtype`, the forward's inputs. Read only.
+ * o       : device, contiguous [B, H, N, d] of `dtype`, the forward's output. Read only.
+ * dout    : device, contiguous [B, H, N, d] of `dtype`. Read only.
+ * lse     : device, contiguous [B, H, N] fp32, the forward's lse. Read only.
+ * dq, dk, dv : device, contiguous [B, H, N, d] of `dtype`; written, rounded to
+ *           nearest-even from fp32.
+ * delta   : device, contiguous [B, H, N] fp32 workspace owned by the caller;
+ *           written with D (the kernels read it back), so it must not be shared
+ *           with a concurrent call.
+ * B, H, N, d, causal, scale, stream, dtype: as for flash_attn_fwd, and they must
+ *           be the values the forward ran with. Requires N * d < 2^31 and
+ *           B * H * ceil(N / 128) < 2^31.
+ *
+ * Ownership, streams and errors as for flash_attn_fwd: nothing is allocated,
+ * three kernels are enqueued on `stream` and nothing is synchronised. Alignment:
+ * the 16-bit tensors 16-byte aligned, lse and delta 4-byte aligned
+ * (FA_ERR_ALIGN). dq, dk, dv and delta must not overlap each other or any input
+ * (FA_ERR_ALIAS).
+ */
+int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, void* dq, void* dk, void* dv, float* delta,
+                   int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
+                   void* stream, int dtype);
+
+/*
+ * flash_attn_bwd_validate -- the argument checks of flash_attn_bwd alone (same
+ * arguments, same status); launches nothing and makes no HIP call.
+ */
+int flash_attn_bwd_validate(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                            const float* lse, void* dq, void* dk, void* dv, float* delta,
+                            int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
+                            void* stream, int dtype);
+
 /* Static, never-freed description of a status code (unknown codes included). */
 const char* flash_attn_strerror(int status);
 
-/* ABI version of this header, currently 1. */
+/* ABI version of this header, currently 2 (1 had the forward pass only). */
 int flash_attn_abi_version(void);
 
 #ifdef __cplusplus

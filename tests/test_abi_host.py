@@ -34,7 +34,8 @@ def _declared_functions():
 def test_library_loads_and_exports_header_symbols():
     assert os.path.exists(LIB_PATH), "build the library first (__graft_entry__.build())"
     names = _declared_functions()
-    assert names == ["flash_attn_abi_version", "flash_attn_fwd", "flash_attn_fwd_validate", "flash_attn_strerror"]
+    assert names == ["flash_attn_abi_version", "flash_attn_bwd", "flash_attn_bwd_validate", "flash_attn_fwd",
+                     "flash_attn_fwd_validate", "flash_attn_strerror"]
     lib = ctypes.CDLL(LIB_PATH)
     for n in names:
         assert hasattr(lib, n)
@@ -44,7 +45,7 @@ def test_library_loads_and_exports_header_symbols():
 
 
 def test_abi_version_and_strerror():
-    assert fa.flash_attn_abi_version() == 1
+    assert fa.flash_attn_abi_version() == 2
     codes = [fa.FA_OK, fa.FA_ERR_NULL, fa.FA_ERR_SHAPE, fa.FA_ERR_HEADDIM, fa.FA_ERR_DTYPE,
              fa.FA_ERR_SCALE, fa.FA_ERR_ALIGN, fa.FA_ERR_ALIAS, fa.FA_ERR_HIP, fa.FA_ERR_ARG]
     msgs = [fa.flash_attn_strerror(c) for c in codes]
@@ -126,3 +127,62 @@ def test_python_binding_rejects_bad_tensors_before_the_library():
         fa.forward(q, q.half(), q)                            # dtype mismatch
     with pytest.raises(TypeError):
         fa._dtype_code(q.float())                             # fp32 is not a kernel dtype
+
+
+# ------------------------------------------------------------------ backward entry point
+def _bargs(q=A, k=A + GB, v=A + 2 * GB, o=A + 3 * GB, dout=A + 4 * GB, lse=A + 5 * GB, dq=A + 6 * GB,
+           dk=A + 7 * GB, dv=A + 8 * GB, delta=A + 9 * GB, B=1, H=1, N=16, d=64, causal=0, scale=0.125,
+           stream=None, dtype=0):
+    return (q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, causal, scale, stream, dtype)
+
+
+BAD_BWD = [
+    (dict(B=-1), fa.FA_ERR_SHAPE), (dict(N=-3), fa.FA_ERR_SHAPE), (dict(d=96), fa.FA_ERR_HEADDIM),
+    (dict(dtype=3), fa.FA_ERR_DTYPE), (dict(causal=5), fa.FA_ERR_ARG), (dict(scale=0.0), fa.FA_ERR_SCALE),
+    (dict(scale=float("nan")), fa.FA_ERR_SCALE),
+    (dict(q=None), fa.FA_ERR_NULL), (dict(o=None), fa.FA_ERR_NULL), (dict(dout=None), fa.FA_ERR_NULL),
+    (dict(lse=None), fa.FA_ERR_NULL), (dict(dq=None), fa.FA_ERR_NULL), (dict(dk=None), fa.FA_ERR_NULL),
+    (dict(dv=None), fa.FA_ERR_NULL), (dict(delta=None), fa.FA_ERR_NULL),
+    (dict(dout=A + 4 * GB + 8), fa.FA_ERR_ALIGN), (dict(dk=A + 7 * GB + 4), fa.FA_ERR_ALIGN),
+    (dict(delta=A + 9 * GB + 2), fa.FA_ERR_ALIGN), (dict(lse=A + 5 * GB + 1), fa.FA_ERR_ALIGN),
+    (dict(dq=A), fa.FA_ERR_ALIAS), (dict(dk=A + 4 * GB + 32), fa.FA_ERR_ALIAS),
+    (dict(dv=A + 6 * GB), fa.FA_ERR_ALIAS), (dict(delta=A + 5 * GB), fa.FA_ERR_ALIAS),
+    (dict(delta=A + 8 * GB + SMALL - 4), fa.FA_ERR_ALIAS), (dict(dq=A + 3 * GB - SMALL + 16), fa.FA_ERR_ALIAS),
+    (dict(N=1 << 24, d=128), fa.FA_ERR_SHAPE), (dict(B=1 << 40, H=1 << 40), fa.FA_ERR_SHAPE),
+]
+
+
+@pytest.mark.parametrize("kw,code", BAD_BWD)
+def test_bwd_validate_rejects(kw, code):
+    assert _native.validate_bwd_raw(*_bargs(**kw)) == code
+    assert _native.bwd_raw(*_bargs(**kw)) == code     # returns before any launch
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(d=128, dtype=1, causal=1), dict(B=2, H=32, N=4096, d=128, causal=1)])
+def test_bwd_validate_accepts(kw):
+    assert _native.validate_bwd_raw(*_bargs(**kw)) == fa.FA_OK
+
+
+def test_bwd_inputs_may_alias_and_outputs_may_touch():
+    """Read-only inputs may share memory; outputs may sit right after one another."""
+    assert _native.validate_bwd_raw(*_bargs(q=A, k=A, v=A, o=A + GB, dout=A + GB)) == fa.FA_OK
+    assert _native.validate_bwd_raw(*_bargs(dq=A + 6 * GB, dk=A + 6 * GB + SMALL, dv=A + 6 * GB + 2 * SMALL,
+                                            delta=A + 6 * GB + 3 * SMALL)) == fa.FA_OK
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(N=0)])
+def test_bwd_empty_problem_is_a_noop(kw):
+    args = _bargs(q=None, k=None, v=None, o=None, dout=None, lse=None, dq=None, dk=None, dv=None, delta=None, **kw)
+    assert _native.validate_bwd_raw(*args) == fa.FA_OK
+    assert _native.bwd_raw(*args) == fa.FA_OK
+
+
+def test_bwd_python_binding_rejects_bad_tensors():
+    import torch
+
+    q = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
+    lse = torch.zeros(1, 2, 8)
+    with pytest.raises(ValueError):
+        fa.backward(q, q, q, q, lse, q)                       # CPU tensors
+    with pytest.raises(ValueError):
+        fa.flash_attn_bwd(q, q, q, q, q, lse.double(), q, q, q, lse)   # lse dtype
