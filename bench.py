@@ -15,7 +15,10 @@ d=128, bf16, inputs resident in HBM. Prints one JSON line:
   workload (a few complete (batch, head) slices) on this host's cores.
 
 Options --workload and --all select other workloads (diagnostics; the JSON line
-keeps the headline workload by default).
+keeps the headline workload by default). --bwd times the backward pass instead
+(one step = one flash_attn_bwd call: D, dQ, dK and dV from Q, K, V, O, LSE and
+dO), counted as 2.5x the forward's FLOPs (five N x N x d products instead of
+two), with the float64 backward oracle as its CPU baseline.
 """
 from __future__ import annotations
 
@@ -34,7 +37,9 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA, vendor figure
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = ["exact_attention_flash_amd/csrc/fwd_kernel.hip", "exact_attention_flash_amd/csrc/fwd_kernel.h"]
+KERNEL_SOURCES = ["exact_attention_flash_amd/csrc/fwd_kernel.hip", "exact_attention_flash_amd/csrc/fwd_kernel.h",
+                  "exact_attention_flash_amd/csrc/gfx950_ops.h"]
+BWD_FLOP_FACTOR = 2.5       # backward: S, dP, dV, dQ, dK products versus the forward's S and PV
 TRAFFIC_FILE = "profiles/fwd_kernel_hbm_traffic.txt"
 
 
@@ -68,7 +73,7 @@ def measured_traffic(workload: str, causal: bool):
     return None
 
 
-def time_gpu(w, causal, steps, warmup):
+def time_gpu(w, causal, steps, warmup, bwd=False):
     import torch
 
     import exact_attention_flash_amd as fa
@@ -82,8 +87,20 @@ def time_gpu(w, causal, steps, warmup):
     scale = inputs.default_scale(w.d)
     stream = torch.cuda.current_stream(dev)
 
-    def step():
+    if bwd:
+        # gradient of the output drawn like the inputs (unit variance), O and LSE
+        # from the forward pass; dQ, dK, dV and the D workspace preallocated
+        dob, _, _ = inputs.workload_qkv(w, seed_offset=7)
+        do = inputs.to_torch(dob, w.dtype, dev)
         fa.flash_attn_fwd(q, k, v, o, lse, causal=causal, scale=scale, stream=stream)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        delta = torch.empty_like(lse)
+
+        def step():
+            fa.flash_attn_bwd(q, k, v, o, do, lse, dq, dk, dv, delta, causal=causal, scale=scale, stream=stream)
+    else:
+        def step():
+            fa.flash_attn_fwd(q, k, v, o, lse, causal=causal, scale=scale, stream=stream)
 
     for _ in range(warmup):
         step()
@@ -153,6 +170,28 @@ def cpu_baseline(w, causal, qkv_bits, slices):
     }
 
 
+def cpu_baseline_bwd(w, causal, qkv_bits, slices):
+    """Time the float64 backward oracle on `slices` complete (batch, head) slices."""
+    from exact_attention_flash_amd import inputs
+    from oracle.backward import attention_backward
+
+    cores = len(os.sched_getaffinity(0))
+    dob, _, _ = inputs.workload_qkv(w, seed_offset=7)
+    qb, kb, vb, db = (x.reshape(-1, w.N, w.d)[:slices] for x in (*qkv_bits, dob))
+    q, k, v, do = (inputs.bits_to_f64(x, w.dtype) for x in (qb, kb, vb, db))
+    t0 = time.perf_counter()
+    attention_backward(q, k, v, do, inputs.default_scale(w.d), causal=causal)
+    dt = time.perf_counter() - t0
+    flops = BWD_FLOP_FACTOR * 4.0 * slices * w.N * w.N * w.d / (2.0 if causal else 1.0)
+    return {
+        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+        "sample": f"{slices} of {w.B * w.H} (batch, head) slices of the same workload, all {w.N} rows, "
+                  f"float64 numpy backward oracle on {cores} host cores; {dt:.1f} s, scaled with the same "
+                  "FLOP formula",
+        "seconds": dt,
+    }
+
+
 def copy_calibration(mib, reps):
     """A plain copy kernel of known size: reads and writes MIB MiB per launch."""
     import torch
@@ -170,6 +209,35 @@ def copy_calibration(mib, reps):
     ms = e0.elapsed_time(e1) / reps
     print(json.dumps({"copy_mib": mib, "bytes_read": n * 4, "bytes_written": n * 4, "ms_per_copy": ms,
                       "GB_per_s": 2 * n * 4 / (ms * 1e-3) / 1e9}), flush=True)
+
+
+def run_bwd(args, workload_name, causal):
+    """Diagnostic line for the backward pass (not the forward's contract line)."""
+    from exact_attention_flash_amd import inputs
+
+    w = inputs.WORKLOADS[workload_name]
+    flops = BWD_FLOP_FACTOR * w.flops(causal)
+    g, qkv = time_gpu(w, causal, args.steps, args.warmup, bwd=True)
+    tflops = flops / (g["ms_per_step"] * 1e-3) / 1e12
+    achieved = flops / (g["event_ms_per_launch"] * 1e-3) / 1e12
+    line = {
+        "metric": "attention bwd TFLOP/s (2.5x forward FLOPs) and % of bf16 MFMA peak",
+        "value": round(tflops, 2), "unit": "TFLOP/s",
+        "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(g["ms_per_step"], 5),
+        "higher_is_better": True, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": causal,
+                   "dtype": w.dtype, "pass": "backward"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "kernel": "bwd_delta + bwd_dq + bwd_dkdv (flash_attn_bwd)", "flop_per_launch": flops,
+                     "launch_ms": round(g["event_ms_per_launch"], 5),
+                     "launch_ms_median": round(g["launch_ms_median"], 5)},
+        "extra_alloc_bytes": g["extra_alloc_bytes"], "device": g["device"],
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_bwd(w, causal, qkv, args.cpu_bwd_slices)
+    return line
 
 
 def run(args, workload_name, causal):
@@ -228,6 +296,9 @@ def main():
     ap.add_argument("--all", action="store_true", help="one line per workload and mask (diagnostics)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-slices", type=int, default=64, help="(batch, head) slices the oracle times")
+    ap.add_argument("--bwd", action="store_true", help="time the backward pass instead (diagnostic line)")
+    ap.add_argument("--cpu-bwd-slices", type=int, default=16,
+                    help="(batch, head) slices the backward oracle times with --bwd")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="only run plain device-to-device copies of MIB MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -246,16 +317,17 @@ def main():
 
     from exact_attention_flash_amd import inputs
 
+    runner = run_bwd if args.bwd else run
     if args.all:
         for name, w in inputs.WORKLOADS.items():
             for c in w.causal:
                 args2 = argparse.Namespace(**vars(args))
                 args2.no_cpu_baseline = True
-                print(json.dumps(run(args2, name, c)), flush=True)
+                print(json.dumps(runner(args2, name, c)), flush=True)
         return
     name = args.workload or inputs.HEADLINE
     causal = inputs.WORKLOADS[name].causal[0] if args.causal is None else bool(args.causal)
-    print(json.dumps(run(args, name, causal)), flush=True)
+    print(json.dumps(runner(args, name, causal)), flush=True)
 
 
 if __name__ == "__main__":
