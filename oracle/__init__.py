@@ -20,6 +20,10 @@ Modules:
   O = P V and LSE = m + ln l, all in float64.
 * ``tiled``  -- a separate online-softmax checker that walks key tiles in any
   order with the (m, l, u) recurrence. It does not import ``dense``.
+* ``backward`` -- dQ, dK, dV and D of the backward pass from their definitions
+  ([V1] §6.1, [IO] "Backward Pass Recomputation").
+* ``splitkv`` -- attention over one key range (a block's O, m, l) and the merge
+  of blocks with the two-block rule of [IO] "Online Softmax Mathematics".
 
 Every function is pinned by tests that do not re-type its formula: the worked
 example printed in [TL], closed forms, invariants, a brute-force fsum evaluation
