@@ -18,7 +18,9 @@ Options --workload and --all select other workloads (diagnostics; the JSON line
 keeps the headline workload by default). --bwd times the backward pass instead
 (one step = one flash_attn_bwd call: D, dQ, dK and dV from Q, K, V, O, LSE and
 dO), counted as 2.5x the forward's FLOPs (five N x N x d products instead of
-two), with the float64 backward oracle as its CPU baseline.
+two), with the float64 backward oracle as its CPU baseline. --splitkv times the
+forward with and without the key split (flash_attn_fwd_splitkv, split count
+planned for this GPU) on the shapes that underfill it.
 """
 from __future__ import annotations
 
@@ -73,7 +75,7 @@ def measured_traffic(workload: str, causal: bool):
     return None
 
 
-def time_gpu(w, causal, steps, warmup, bwd=False):
+def time_gpu(w, causal, steps, warmup, bwd=False, splits=None):
     import torch
 
     import exact_attention_flash_amd as fa
@@ -87,7 +89,14 @@ def time_gpu(w, causal, steps, warmup, bwd=False):
     scale = inputs.default_scale(w.d)
     stream = torch.cuda.current_stream(dev)
 
-    if bwd:
+    if splits is not None:
+        nbytes = fa.splitkv_workspace_size(w.B, w.H, w.N, w.d, causal, splits)
+        ws = torch.empty(max(nbytes // 4, 1), dtype=torch.float32, device=dev) if nbytes else None
+
+        def step():
+            fa.flash_attn_fwd_splitkv(q, k, v, o, lse, ws, causal=causal, scale=scale, num_splits=splits,
+                                      stream=stream)
+    elif bwd:
         # gradient of the output drawn like the inputs (unit variance), O and LSE
         # from the forward pass; dQ, dK, dV and the D workspace preallocated
         dob, _, _ = inputs.workload_qkv(w, seed_offset=7)
@@ -240,6 +249,38 @@ def run_bwd(args, workload_name, causal):
     return line
 
 
+def run_splitkv(args):
+    """Diagnostic lines: forward with and without the key split on underfilled shapes."""
+    import torch
+
+    import exact_attention_flash_amd as fa
+    from exact_attention_flash_amd import inputs
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    names = list(inputs.SPLIT_WORKLOADS) + ["single_head_n256_d64", "mha_b4_h16_n1024_d64"]
+    for name in names:
+        w = inputs.SPLIT_WORKLOADS.get(name) or inputs.WORKLOADS[name]
+        causal = w.causal[0]
+        flops = w.flops(causal)
+        splits = fa.splitkv_plan(w.B, w.H, w.N, w.d, causal, cus)
+        plain, _ = time_gpu(w, causal, args.steps, args.warmup)
+        split, _ = time_gpu(w, causal, args.steps, args.warmup, splits=splits)
+        items = w.B * w.H * -(-w.N // 256)
+        line = {
+            "metric": "attention fwd TFLOP/s, key split versus plain (diagnostic)",
+            "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": causal,
+                       "dtype": w.dtype, "work_items": items, "compute_units": cus, "splits": splits},
+            "plain": {"launch_ms": round(plain["event_ms_per_launch"], 5),
+                      "tflops": round(flops / (plain["event_ms_per_launch"] * 1e-3) / 1e12, 2)},
+            "splitkv": {"launch_ms": round(split["event_ms_per_launch"], 5),
+                        "tflops": round(flops / (split["event_ms_per_launch"] * 1e-3) / 1e12, 2),
+                        "note": "split kernel + merge kernel, one call"},
+            "speedup": round(plain["event_ms_per_launch"] / split["event_ms_per_launch"], 3),
+            "unit": "TFLOP/s", "steps": args.steps, "warmup": args.warmup,
+        }
+        print(json.dumps(line), flush=True)
+
+
 def run(args, workload_name, causal):
     from exact_attention_flash_amd import inputs
 
@@ -297,6 +338,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-slices", type=int, default=64, help="(batch, head) slices the oracle times")
     ap.add_argument("--bwd", action="store_true", help="time the backward pass instead (diagnostic line)")
+    ap.add_argument("--splitkv", action="store_true",
+                    help="time the key-split forward against the plain one on underfilled shapes (diagnostic)")
     ap.add_argument("--cpu-bwd-slices", type=int, default=16,
                     help="(batch, head) slices the backward oracle times with --bwd")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
@@ -317,6 +360,9 @@ def main():
 
     from exact_attention_flash_amd import inputs
 
+    if args.splitkv:
+        run_splitkv(args)
+        return
     runner = run_bwd if args.bwd else run
     if args.all:
         for name, w in inputs.WORKLOADS.items():

@@ -11,9 +11,11 @@ import math
 
 from . import _native
 from ._native import (FA_BF16, FA_FP16, FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEADDIM,  # noqa: F401
-                      FA_ERR_DTYPE, FA_ERR_SCALE, FA_ERR_ALIGN, FA_ERR_ALIAS, FA_ERR_HIP, FA_ERR_ARG)
+                      FA_ERR_DTYPE, FA_ERR_SCALE, FA_ERR_ALIGN, FA_ERR_ALIAS, FA_ERR_HIP, FA_ERR_ARG,
+                      FA_ERR_WORKSPACE)
 
-__all__ = ["forward", "backward", "flash_attn_fwd", "flash_attn_bwd", "flash_attn_strerror", "flash_attn_abi_version"]
+__all__ = ["forward", "backward", "forward_splitkv", "flash_attn_fwd", "flash_attn_fwd_splitkv", "flash_attn_bwd",
+           "splitkv_plan", "splitkv_workspace_size", "flash_attn_strerror", "flash_attn_abi_version"]
 
 
 class FlashAttnError(RuntimeError):
@@ -76,6 +78,91 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, stream=No
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     flash_attn_fwd(q, k, v, o, lse, causal=causal, scale=scale, stream=stream)
     return o, lse
+
+
+def _check_fwd_tensors(q, k, v, o, lse):
+    import torch
+
+    if q.dim() != 4:
+        raise ValueError("q must have shape [B, H, N, d]")
+    for name, t in (("k", k), ("v", v), ("o", o)):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{name} must match q in shape and dtype")
+    B, H, N, _ = q.shape
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 with shape [B, H, N]")
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.device != q.device:
+            raise ValueError("all tensors must be on one device")
+
+
+def splitkv_plan(B: int, H: int, N: int, d: int, causal: bool, cus: int) -> int:
+    """Split count the library chooses for a device with ``cus`` compute units."""
+    st = _native.splitkv_plan(B, H, N, d, causal, cus)
+    if st < 1:
+        raise FlashAttnError(st, "flash_attn_fwd_splitkv_plan")
+    return st
+
+
+def splitkv_workspace_size(B: int, H: int, N: int, d: int, causal: bool, num_splits: int) -> int:
+    """Workspace bytes flash_attn_fwd_splitkv needs for ``num_splits`` (>= 1)."""
+    st = _native.splitkv_workspace_size(B, H, N, d, causal, num_splits)
+    if st < 0:
+        raise FlashAttnError(int(st), "flash_attn_fwd_splitkv_workspace_size")
+    return int(st)
+
+
+def flash_attn_fwd_splitkv(q, k, v, o, lse, workspace, causal: bool = False, scale: float | None = None,
+                           num_splits: int = 0, stream=None) -> None:
+    """The key-split forward on caller-owned tensors (the C entry point with torch arguments).
+
+    workspace: a CUDA tensor (any dtype, contiguous) of at least
+    splitkv_workspace_size(...) bytes for the resolved split count, or None when
+    that count is 1.
+    """
+    import torch
+
+    _check_fwd_tensors(q, k, v, o, lse)
+    B, H, N, d = q.shape
+    dtype = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    if workspace is None:
+        ws, ws_bytes = 0, 0
+    else:
+        if not workspace.is_cuda or not workspace.is_contiguous() or workspace.device != q.device:
+            raise ValueError("workspace must be a contiguous GPU tensor on q's device")
+        ws, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    st = _native.splitkv_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                             B, H, N, d, causal, scale, num_splits, ws, ws_bytes, stream.cuda_stream, dtype)
+    if st != FA_OK:
+        raise FlashAttnError(st, "flash_attn_fwd_splitkv")
+
+
+def forward_splitkv(q, k, v, causal: bool = False, scale: float | None = None, num_splits: int = 0,
+                    stream=None):
+    """Allocate O, LSE and the split workspace and run the key-split forward. Returns
+    (o, lse, splits) with the split count used. num_splits = 0 lets the library
+    choose from the device's compute-unit count."""
+    import torch
+
+    B, H, N, d = q.shape
+    if num_splits == 0:
+        cus = torch.cuda.get_device_properties(q.device).multi_processor_count
+        num_splits = splitkv_plan(B, H, N, d, causal, cus)
+    nbytes = splitkv_workspace_size(B, H, N, d, causal, num_splits)
+    ws = torch.empty(max(nbytes // 4, 1), dtype=torch.float32, device=q.device) if nbytes else None
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    flash_attn_fwd_splitkv(q, k, v, o, lse, ws, causal=causal, scale=scale, num_splits=num_splits, stream=stream)
+    splits = nbytes // max(1, B * H * N * (d + 1) * 4) if nbytes else 1
+    return o, lse, splits
 
 
 def flash_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, causal: bool = False, scale: float | None = None,

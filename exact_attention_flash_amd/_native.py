@@ -19,6 +19,7 @@ FA_ERR_ALIGN = -6
 FA_ERR_ALIAS = -7
 FA_ERR_HIP = -8
 FA_ERR_ARG = -9
+FA_ERR_WORKSPACE = -10
 
 _lib = None
 
@@ -40,6 +41,19 @@ def lib() -> ctypes.CDLL:
         ]
         L.flash_attn_fwd_validate.restype = ctypes.c_int
         L.flash_attn_fwd_validate.argtypes = L.flash_attn_fwd.argtypes
+        L.flash_attn_fwd_splitkv.restype = ctypes.c_int
+        L.flash_attn_fwd_splitkv.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_uint64,
+            ctypes.c_void_p, ctypes.c_int,
+        ]
+        L.flash_attn_fwd_splitkv_validate.restype = ctypes.c_int
+        L.flash_attn_fwd_splitkv_validate.argtypes = L.flash_attn_fwd_splitkv.argtypes
+        L.flash_attn_fwd_splitkv_plan.restype = ctypes.c_int
+        L.flash_attn_fwd_splitkv_plan.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int, ctypes.c_int]
+        L.flash_attn_fwd_splitkv_workspace_size.restype = ctypes.c_int64
+        L.flash_attn_fwd_splitkv_workspace_size.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int, ctypes.c_int]
         L.flash_attn_bwd.restype = ctypes.c_int
         L.flash_attn_bwd.argtypes = [ctypes.c_void_p] * 10 + [
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
@@ -63,6 +77,27 @@ def fwd_raw(q, k, v, o, lse, B, H, N, d, causal, scale, stream, dtype) -> int:
 def validate_raw(q, k, v, o, lse, B, H, N, d, causal, scale, stream, dtype) -> int:
     """Call flash_attn_fwd_validate (host checks only, never launches)."""
     return lib().flash_attn_fwd_validate(q, k, v, o, lse, B, H, N, d, int(causal), float(scale), stream, dtype)
+
+
+def splitkv_raw(q, k, v, o, lse, B, H, N, d, causal, scale, num_splits, ws, ws_bytes, stream, dtype) -> int:
+    """Call flash_attn_fwd_splitkv with integer addresses; returns the status code."""
+    return lib().flash_attn_fwd_splitkv(q, k, v, o, lse, B, H, N, d, int(causal), float(scale), int(num_splits),
+                                        ws, int(ws_bytes), stream, dtype)
+
+
+def validate_splitkv_raw(q, k, v, o, lse, B, H, N, d, causal, scale, num_splits, ws, ws_bytes, stream,
+                         dtype) -> int:
+    """Call flash_attn_fwd_splitkv_validate (host checks only, never launches)."""
+    return lib().flash_attn_fwd_splitkv_validate(q, k, v, o, lse, B, H, N, d, int(causal), float(scale),
+                                                 int(num_splits), ws, int(ws_bytes), stream, dtype)
+
+
+def splitkv_plan(B, H, N, d, causal, cus) -> int:
+    return lib().flash_attn_fwd_splitkv_plan(B, H, N, d, int(causal), int(cus))
+
+
+def splitkv_workspace_size(B, H, N, d, causal, num_splits) -> int:
+    return lib().flash_attn_fwd_splitkv_workspace_size(B, H, N, d, int(causal), int(num_splits))
 
 
 def bwd_raw(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, causal, scale, stream, dtype) -> int:

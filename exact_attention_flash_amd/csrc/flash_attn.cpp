@@ -22,7 +22,7 @@ bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p
 
 }  // namespace
 
-extern "C" int flash_attn_abi_version(void) { return 2; }
+extern "C" int flash_attn_abi_version(void) { return 3; }
 
 extern "C" const char* flash_attn_strerror(int status) {
   switch (status) {
@@ -35,7 +35,8 @@ extern "C" const char* flash_attn_strerror(int status) {
     case FA_ERR_ALIGN: return "16-bit tensors must be 16-byte aligned and fp32 ones 4-byte aligned";
     case FA_ERR_ALIAS: return "an output overlaps an input or another output";
     case FA_ERR_HIP: return "HIP runtime error at launch";
-    case FA_ERR_ARG: return "causal must be 0 or 1";
+    case FA_ERR_ARG: return "causal must be 0 or 1, and num_splits >= 0";
+    case FA_ERR_WORKSPACE: return "workspace is NULL, misaligned or smaller than the split needs";
     default: return "unknown status";
   }
 }
@@ -87,6 +88,73 @@ int check_args(const void* q, const void* k, const void* v, void* o, float* lse,
   a->grid = static_cast<int>(bh * q_tiles);
   a->xcd_grouped = (bh % 8 == 0) ? 1 : 0;
   a->scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634074);
+  a->splits = 1;
+  a->part_o = nullptr;
+  a->part_lse = nullptr;
+  return FA_OK;
+}
+
+// ---- key split ----
+constexpr int kMaxSplits = 16;
+
+// Largest split count for which no work item is empty: the fewest key tiles any
+// query tile visits (causal: the first query tile's), capped at kMaxSplits.
+int max_splits(int64_t N, int causal) {
+  const int64_t bn = fa::keys_per_tile(), bm = fa::rows_per_workgroup();
+  const int64_t tiles_all = (N + bn - 1) / bn;
+  int64_t fewest = tiles_all;
+  if (causal) {
+    const int64_t first = ((N < bm ? N : bm) - 1) / bn + 1;
+    if (first < fewest) fewest = first;
+  }
+  if (fewest > kMaxSplits) fewest = kMaxSplits;
+  return fewest < 1 ? 1 : static_cast<int>(fewest);
+}
+
+int resolve_splits(int64_t N, int causal, int num_splits) {
+  const int mx = max_splits(N, causal);
+  return num_splits > mx ? mx : num_splits;
+}
+
+// Split count for a device with `cus` compute units: enough items to give every
+// compute unit one, when the unsplit work has fewer items than compute units and
+// the sequence spans at least kMinSplitTiles key tiles (below that an item is so
+// short that the merge launch costs more than the split saves).
+constexpr int kMinSplitTiles = 8;
+
+int plan_splits(int64_t bh, int64_t N, int causal, int cus) {
+  const int64_t items = bh * ((N + fa::rows_per_workgroup() - 1) / fa::rows_per_workgroup());
+  if (items <= 0 || cus <= 0 || items >= cus) return 1;
+  if ((N + fa::keys_per_tile() - 1) / fa::keys_per_tile() < kMinSplitTiles) return 1;
+  const int64_t want = (cus + items - 1) / items;
+  return resolve_splits(N, causal, want > kMaxSplits ? kMaxSplits : static_cast<int>(want));
+}
+
+uint64_t workspace_bytes_for(int64_t bh, int64_t N, int64_t d, int splits) {
+  if (splits <= 1) return 0;
+  return static_cast<uint64_t>(splits) * static_cast<uint64_t>(bh) * static_cast<uint64_t>(N) *
+         static_cast<uint64_t>(d + 1) * 4u;
+}
+
+// Checks of the split call beyond those of the forward; fills the split fields.
+// num_splits must already be resolved (>= 1).
+int check_split(const void* q, const void* k, const void* v, const void* o, const float* lse, int64_t B,
+                int64_t H, int64_t N, int64_t d, int splits, void* workspace, uint64_t workspace_bytes,
+                fa::FwdArgs* a) {
+  if (splits <= 1) return FA_OK;
+  const int64_t bh = B * H;
+  if (static_cast<int64_t>(a->q_tiles) * bh > INT32_MAX / splits) return FA_ERR_SHAPE;
+  const uint64_t need = workspace_bytes_for(bh, N, d, splits);
+  if (!workspace || !aligned(workspace, 16) || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  const uint64_t in_bytes = static_cast<uint64_t>(bh) * N * d * 2;
+  const uint64_t lse_bytes = static_cast<uint64_t>(bh) * N * 4;
+  if (overlaps(workspace, need, q, in_bytes) || overlaps(workspace, need, k, in_bytes) ||
+      overlaps(workspace, need, v, in_bytes) || overlaps(workspace, need, o, in_bytes) ||
+      overlaps(workspace, need, lse, lse_bytes))
+    return FA_ERR_ALIAS;
+  a->splits = splits;
+  a->part_o = static_cast<float*>(workspace);
+  a->part_lse = static_cast<float*>(workspace) + static_cast<uint64_t>(splits) * bh * N * d;
   return FA_OK;
 }
 
@@ -106,6 +174,67 @@ extern "C" int flash_attn_fwd(const void* q, const void* k, const void* v, void*
   fa::FwdArgs a;
   bool empty;
   const int st = check_args(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, &a, &empty);
+  if (st != FA_OK || empty) return st;
+  const hipError_t err = fa::launch_fwd(a, dtype == FA_FP16, static_cast<int>(d), causal == 1,
+                                        static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+extern "C" int flash_attn_fwd_splitkv_plan(int64_t B, int64_t H, int64_t N, int64_t d, int causal, int cus) {
+  if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  if (B == 0 || H == 0 || N == 0) return 1;
+  if (B > INT32_MAX / H) return FA_ERR_SHAPE;
+  return plan_splits(B * H, N, causal, cus);
+}
+
+extern "C" int64_t flash_attn_fwd_splitkv_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, int causal,
+                                                         int num_splits) {
+  if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if ((causal != 0 && causal != 1) || num_splits < 1) return FA_ERR_ARG;
+  if (B == 0 || H == 0 || N == 0) return 0;
+  if (B > INT32_MAX / H) return FA_ERR_SHAPE;
+  return static_cast<int64_t>(workspace_bytes_for(B * H, N, d, resolve_splits(N, causal, num_splits)));
+}
+
+namespace {
+
+int splitkv_common(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                   int64_t N, int64_t d, int causal, float scale, int num_splits, void* workspace,
+                   uint64_t workspace_bytes, int dtype, bool plan_on_device, fa::FwdArgs* a, bool* empty) {
+  if (num_splits < 0) return FA_ERR_ARG;
+  const int st = check_args(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, a, empty);
+  if (st != FA_OK || *empty) return st;
+  int splits = num_splits;
+  if (splits == 0) {
+    if (!plan_on_device) return FA_OK;  // validation only: the split is chosen at launch
+    splits = plan_splits(a->bh, N, causal, fa::device_cus());
+  }
+  splits = resolve_splits(N, causal, splits);
+  return check_split(q, k, v, o, lse, B, H, N, d, splits, workspace, workspace_bytes, a);
+}
+
+}  // namespace
+
+extern "C" int flash_attn_fwd_splitkv_validate(const void* q, const void* k, const void* v, void* o, float* lse,
+                                               int64_t B, int64_t H, int64_t N, int64_t d, int causal,
+                                               float scale, int num_splits, void* workspace,
+                                               uint64_t workspace_bytes, void* /*stream*/, int dtype) {
+  fa::FwdArgs a;
+  bool empty;
+  return splitkv_common(q, k, v, o, lse, B, H, N, d, causal, scale, num_splits, workspace, workspace_bytes, dtype,
+                        false, &a, &empty);
+}
+
+extern "C" int flash_attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                                      int64_t H, int64_t N, int64_t d, int causal, float scale, int num_splits,
+                                      void* workspace, uint64_t workspace_bytes, void* stream, int dtype) {
+  fa::FwdArgs a;
+  bool empty;
+  const int st = splitkv_common(q, k, v, o, lse, B, H, N, d, causal, scale, num_splits, workspace,
+                                workspace_bytes, dtype, true, &a, &empty);
   if (st != FA_OK || empty) return st;
   const hipError_t err = fa::launch_fwd(a, dtype == FA_FP16, static_cast<int>(d), causal == 1,
                                         static_cast<hipStream_t>(stream));

@@ -17,13 +17,27 @@ struct FwdArgs {
   int grid;         // workgroups launched (persistent: at most one per CU)
   int xcd_grouped;  // 1 when bh % 8 == 0: keep each slice's tiles on one XCD
   float scale_log2; // scale * log2(e)
+  // key split (splits > 1): every query tile's key tiles are cut into `splits`
+  // contiguous ranges handled as separate work items; each writes its normalised
+  // partial output and log-sum-exp (fp32) to part_o [splits, bh, n, d] and
+  // part_lse [splits, bh, n], and a merge kernel forms o and lse from them
+  int splits;
+  float* part_o;
+  float* part_lse;
 };
 
 // Query rows handled by one workgroup.
 int rows_per_workgroup();
 
+// Keys per streamed tile.
+int keys_per_tile();
+
+// Compute units of the current device (queried once per device), or 0 on error.
+int device_cus();
+
 // Enqueue the kernel instance for (dtype, d, causal); d is 64 or 128. Sizes the
-// persistent grid from the current device's compute units.
+// persistent grid from the current device's compute units. With a.splits > 1 the
+// split instance runs and is followed by the merge kernel.
 hipError_t launch_fwd(const FwdArgs& a, bool fp16, int d, bool causal, hipStream_t stream);
 
 }  // namespace fa

@@ -43,6 +43,15 @@
 //  * Item order: heaviest causal query tiles first, dealt to the workgroups in
 //    snake order so that every workgroup gets the same causal work; all query
 //    tiles of one (batch, head) on one XCD so K/V tiles are shared through its L2.
+//  * Key split (shapes with fewer work items than compute units): the key tiles a
+//    query tile visits are cut into S contiguous ranges, each its own work item.
+//    An item's rows end with the range's own (m, l, u); it stores u / l and
+//    m + ln l in fp32, and merge_splits combines the S partials of a row with the
+//    two-block rule of the IO-aware tiling page ("Online Softmax Mathematics"):
+//    m = max m_k, l = sum e^(m_k - m) l_k, O = sum (l_k e^(m_k - m) / l) O_k,
+//    written with the identity l_k e^(m_k - m) / l = e^(LSE_k - LSE). A causal
+//    row that ends before its range starts has l = 0 there and stores O = 0 and
+//    LSE = -inf (weight zero in the merge).
 //
 // Reference maximum. The rescaling identity of "6.1 FlashAttention V1 in detail",
 // §3.3 holds for any per-row reference r: with p = 2^(s' - r) (s' the score in
@@ -91,7 +100,7 @@ struct Geo {
   __device__ static __forceinline__ int swz(int row) { return chunk_swizzle<D>(row); }
 };
 
-template <bool FP16, int D, bool CAUSAL>
+template <bool FP16, int D, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
   using G = Geo<D>;
   __shared__ __attribute__((aligned(1024))) char smem[kStages * G::stageBytes + G::qBytes];
@@ -124,7 +133,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
     wg_n = (int)gridDim.x;
     bh_base = 0;
   }
-  const int n_items = hpx * a.q_tiles;
+  const int splits = SPLIT ? a.splits : 1;
+  const int n_items = hpx * a.q_tiles * splits;
   const int N = a.n;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
   const int tiles_all = (N + kBN - 1) / kBN;
@@ -133,11 +143,21 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
     const int j = r * wg_n + ((r & 1) ? wg_n - 1 - wg_k : wg_k);
     return j < n_items ? j : -1;
   };
+  // item j: slice j % hpx; query-tile rank and key split from j / hpx (the splits
+  // of one query tile are adjacent in the ranked list)
   auto item_bh = [&](int j) { return bh_base + j % hpx; };
-  auto item_q0 = [&](int j) { return (CAUSAL ? (a.q_tiles - 1 - j / hpx) : j / hpx) * kBM; };
+  auto item_rank = [&](int j) { return SPLIT ? (j / hpx) / splits : j / hpx; };
+  auto item_split = [&](int j) { return SPLIT ? (j / hpx) % splits : 0; };
+  auto item_q0 = [&](int j) { return (CAUSAL ? (a.q_tiles - 1 - item_rank(j)) : item_rank(j)) * kBM; };
   // key tiles visited by a query tile starting at q0 (causal: up to its last row)
   auto item_tiles = [&](int q0) {
     return CAUSAL ? min(tiles_all, (min(q0 + kBM, N) - 1) / kBN + 1) : tiles_all;
+  };
+  // key tiles [item_first, item_last) of item j: split s of the query tile's nt
+  // tiles is [s nt / S, (s + 1) nt / S), never empty because S <= nt
+  auto item_first = [&](int j) { return SPLIT ? item_split(j) * item_tiles(item_q0(j)) / splits : 0; };
+  auto item_last = [&](int j) {
+    return SPLIT ? (item_split(j) + 1) * item_tiles(item_q0(j)) / splits : item_tiles(item_q0(j));
   };
   // this wave's block of 32 rows: block wave%4 (group A) or 7 - wave%4 (group B)
   const int wave_rows = 32 * (grp == 0 ? (wave & 3) : 7 - (wave & 3));
@@ -163,8 +183,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
     const int64_t off = (int64_t)item_bh(c_j) * N * D;
     c_k = reinterpret_cast<const uint16_t*>(a.k) + off;
     c_v = reinterpret_cast<const uint16_t*>(a.v) + off;
-    c_n = item_tiles(item_q0(c_j));
-    c_t = 0;
+    c_n = item_last(c_j);
+    c_t = item_first(c_j);
   };
   cursor_item();
   // issue the cursor's tile and advance; false once the stream is exhausted
@@ -251,9 +271,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
 
   // the current item: its first row, this wave's rows, its key tiles and the
   // stream index of its tile 0
+  // (with a key split, tile i of the item is key tile t_base + i)
   int it_r = 0, it_j = first_j;
-  int row0 = 0, qrow = 0, n_tiles = 0, g0 = 0;
-  auto active = [&](int t) { return row0 < N && (!CAUSAL || t * kBN <= row0 + 31); };
+  int row0 = 0, qrow = 0, n_tiles = 0, g0 = 0, t_base = 0;
+  auto key_tile = [&](int t) { return SPLIT ? t_base + t : t; };
+  auto active = [&](int t) { return row0 < N && (!CAUSAL || key_tile(t) * kBN <= row0 + 31); };
 
   // per-lane K offsets: row l32 (the second block of 32 keys adds 32 rows), logical
   // chunk 2*kk + h
@@ -321,7 +343,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
   // sum run as four independent chains to keep the VALU pipeline full.
   auto softmax_phase = [&](int t) {
     if (!(t >= 0 && t < n_tiles && active(t))) return;
-    const int kv0 = t * kBN;
+    const int kv0 = key_tile(t) * kBN;
     if ((kv0 + kBN > N) || (CAUSAL && kv0 + kBN - 1 > row0)) {
       // key = kv0 + c(b, r) + 4h with c(b, r) = 32b + 8(r/4) + r%4; a key is dead
       // past the sequence end or (causal) after the query: c(b, r) > lim
@@ -403,7 +425,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
     const int bh = item_bh(it_j);
     row0 = item_q0(it_j) + wave_rows;
     qrow = row0 + l32;
-    n_tiles = item_tiles(item_q0(it_j));
+    if constexpr (SPLIT) {
+      t_base = item_first(it_j);
+      n_tiles = item_last(it_j) - t_base;
+    } else {
+      n_tiles = item_tiles(item_q0(it_j));
+    }
     const int next_j = item_index(it_r + 1);
     m_run = -INFINITY;
     l_run = 0.f;
@@ -445,7 +472,24 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
     // here, before the stores, so that the next item need not wait for the stores
     wait_vmcnt<0>();
     const float l_tot = l_run + other_half(l_run);
-    if (qrow < N) {
+    if (SPLIT && qrow < N) {
+      // partial of this key range: u / l and m + ln l in fp32 (a row with no
+      // visible key in the range has l = 0: O = 0, LSE = -inf)
+      const int64_t prow = ((int64_t)item_split(it_j) * a.bh + bh) * N + qrow;
+      const bool live = l_tot > 0.f;
+      const float inv = live ? 1.0f / l_tot : 0.f;
+      float* po = a.part_o + prow * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<f32x4*>(po + db * 32 + 8 * g + 4 * h) =
+              f32x4{acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv, acc[db][4 * g + 2] * inv,
+                    acc[db][4 * g + 3] * inv};
+      if (h == 0)
+        a.part_lse[prow] = live ? (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994530942f : -INFINITY;
+    }
+    if (!SPLIT && qrow < N) {
       const float inv = 1.0f / l_tot;
       uint16_t* og = reinterpret_cast<uint16_t*>(a.o) + (int64_t)bh * N * D + (int64_t)qrow * D;
 #pragma unroll
@@ -465,14 +509,53 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
   }
 }
 
+// Merge of the key-split partials of every row (memory bound): D/4 lanes per row,
+// four fp32 columns per lane. LSE = M + ln sum_k e^(LSE_k - M) with M = max_k LSE_k
+// (finite: split 0 holds key 0, which every row sees), O = sum_k e^(LSE_k - LSE) O_k,
+// rounded to the output dtype.
+template <bool FP16, int D>
+__global__ __launch_bounds__(256) void merge_splits(FwdArgs a) {
+  constexpr int kLanes = D / 4;
+  constexpr int kRows = 256 / kLanes;
+  const int64_t rows = (int64_t)a.bh * a.n;
+  const int64_t row = (int64_t)blockIdx.x * kRows + threadIdx.x / kLanes;
+  const int c = threadIdx.x % kLanes;
+  if (row >= rows) return;
+  const int S = a.splits;
+  float mx = -INFINITY;
+  for (int k = 0; k < S; ++k) mx = fmaxf(mx, a.part_lse[k * rows + row]);
+  float den = 0.f;
+  for (int k = 0; k < S; ++k) den += expf(a.part_lse[k * rows + row] - mx);
+  const float lse = mx + logf(den);
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < S; ++k) {
+    const float w = expf(a.part_lse[k * rows + row] - lse);
+    const f32x4 x = *reinterpret_cast<const f32x4*>(a.part_o + (k * rows + row) * D + 4 * c);
+    o += w * x;
+  }
+  uint16_t* og = reinterpret_cast<uint16_t*>(a.o) + row * D + 4 * c;
+  *reinterpret_cast<u32x2*>(og) = u32x2{pack2<FP16>(o[0], o[1]), pack2<FP16>(o[2], o[3])};
+  if (c == 0) a.lse[row] = lse;
+}
+
 template <bool FP16, int D, bool CAUSAL>
 hipError_t launch_one(const FwdArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((fwd_pingpong<FP16, D, CAUSAL>), dim3(a.grid), dim3(kThreads), 0, stream, a);
+  if (a.splits > 1) {
+    hipLaunchKernelGGL((fwd_pingpong<FP16, D, CAUSAL, true>), dim3(a.grid), dim3(kThreads), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    constexpr int kRows = 256 / (D / 4);
+    const int64_t rows = (int64_t)a.bh * a.n;
+    hipLaunchKernelGGL((merge_splits<FP16, D>), dim3((unsigned)((rows + kRows - 1) / kRows)), dim3(256), 0, stream,
+                       a);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((fwd_pingpong<FP16, D, CAUSAL, false>), dim3(a.grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 // compute units of the current device, queried once per device
-int device_cus() {
+int cached_cus() {
   static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
@@ -489,6 +572,8 @@ int device_cus() {
 }  // namespace pp
 
 int rows_per_workgroup() { return pp::kBM; }
+int keys_per_tile() { return pp::kBN; }
+int device_cus() { return pp::cached_cus(); }
 
 hipError_t launch_fwd(const FwdArgs& args, bool fp16, int d, bool causal, hipStream_t stream) {
   using namespace pp;
@@ -498,8 +583,8 @@ hipError_t launch_fwd(const FwdArgs& args, bool fp16, int d, bool causal, hipStr
   FwdArgs a = args;
   const int cus = device_cus();
   if (cus <= 0) return hipErrorInvalidDevice;
-  int grid = a.bh * a.q_tiles;
-  if (grid > cus) grid = cus;
+  const int64_t items = (int64_t)a.bh * a.q_tiles * (a.splits > 1 ? a.splits : 1);
+  int grid = items < cus ? (int)items : cus;
   if (a.xcd_grouped) {
     grid &= ~7;
     if (grid < 8) grid = 8;

@@ -66,6 +66,15 @@ WORKLOADS = {
 }
 HEADLINE = "llama7b_b2_h32_n4096_d128_causal"
 
+# Shapes with fewer (batch, head, 256-row query tile) work items than the GPU has
+# compute units, where the key-split forward applies: a few heads of a long causal
+# sequence (e.g. one tensor-parallel shard's heads) and one long non-causal head.
+SPLIT_WORKLOADS = {
+    "few_heads_b1_h4_n4096_d128_causal": Workload(
+        "few_heads_b1_h4_n4096_d128_causal", 1, 4, 4096, 128, BF16, 1.0, (True,), 6),
+    "one_head_b1_h1_n8192_d128": Workload("one_head_b1_h1_n8192_d128", 1, 1, 8192, 128, BF16, 1.0, (False,), 7),
+}
+
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 to bfloat16 (round-to-nearest-even); return uint16 bits.

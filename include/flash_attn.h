@@ -43,7 +43,8 @@ typedef enum {
   FA_ERR_ALIGN = -6,   /* a 16-bit tensor not 16-byte aligned, or an fp32 one not 4-byte aligned */
   FA_ERR_ALIAS = -7,   /* an output overlaps an input or another output          */
   FA_ERR_HIP = -8,     /* the HIP runtime reported an error at launch             */
-  FA_ERR_ARG = -9      /* causal is not 0 or 1                                    */
+  FA_ERR_ARG = -9,     /* causal is not 0 or 1, or num_splits is negative        */
+  FA_ERR_WORKSPACE = -10 /* split workspace NULL, not 16-byte aligned or too small */
 } fa_status;
 
 /*
@@ -89,6 +90,76 @@ int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* 
 int flash_attn_fwd_validate(const void* q, const void* k, const void* v, void* o, float* lse,
                             int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
                             void* stream, int dtype);
+
+/*
+ * flash_attn_fwd_splitkv -- the forward pass with every query tile's keys cut
+ * into num_splits contiguous ranges processed as separate work items, for shapes
+ * with fewer (batch, head, 256-row query tile) items than the GPU has compute
+ * units. Each range produces, per query row, its own softmax statistics and
+ * normalised output; a second kernel merges the ranges of each row with the
+ * two-block rule of "FlashAttention: IO-Aware Tiling, Online Softmax
+ * Mathematics, Memory Hierarchy Dynamics, and Kernel Evolution", section
+ * "Online Softmax Mathematics" (m = max(m1, m2), l = e^(m1-m) l1 + e^(m2-m) l2,
+ * O = (l1 e^(m1-m) / l) O1 + (e^(m2-m) / l) P2 V2), applied to all ranges at once.
+ * The result is the same attention as flash_attn_fwd (o and lse as documented
+ * there), up to rounding.
+ *
+ * Arguments q, k, v, o, lse, B, H, N, d, causal, scale, stream, dtype: as for
+ * flash_attn_fwd.
+ * num_splits : ranges per query tile. 0 chooses with flash_attn_fwd_splitkv_plan
+ *           for the current device; values above the largest useful count (no
+ *           empty range: the fewest 64-key tiles any query tile visits, at most
+ *           16) are reduced to it. A resolved count of 1 runs flash_attn_fwd and
+ *           leaves the workspace untouched (it may then be NULL).
+ * workspace : device memory owned by the caller, 16-byte aligned, at least
+ *           flash_attn_fwd_splitkv_workspace_size(...) bytes for the resolved
+ *           count S. On return it holds fp32 partial outputs [S, B*H, N, d]
+ *           followed by fp32 partial log-sum-exps [S, B*H, N] (range s of a row:
+ *           its keys' normalised output and ln of its sum of exp(scores); a row
+ *           with no visible key in the range has output 0 and -inf). It must not
+ *           overlap q, k, v, o or lse (FA_ERR_ALIAS) and must not be shared with
+ *           a concurrent call.
+ * workspace_bytes : size of workspace in bytes (FA_ERR_WORKSPACE if too small).
+ *
+ * Ownership, streams and errors as for flash_attn_fwd (two kernels are enqueued
+ * on `stream` when S > 1). With num_splits = 0 the call queries the current
+ * device's compute-unit count (one HIP attribute query per device, cached).
+ * Requires B * H * ceil(N / 256) * S < 2^31.
+ */
+int flash_attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
+                           int num_splits, void* workspace, uint64_t workspace_bytes,
+                           void* stream, int dtype);
+
+/*
+ * flash_attn_fwd_splitkv_validate -- the checks of flash_attn_fwd_splitkv alone;
+ * no HIP call. With num_splits = 0 the workspace is not checked (the count is
+ * chosen at launch).
+ */
+int flash_attn_fwd_splitkv_validate(const void* q, const void* k, const void* v, void* o, float* lse,
+                                    int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
+                                    int num_splits, void* workspace, uint64_t workspace_bytes,
+                                    void* stream, int dtype);
+
+/*
+ * flash_attn_fwd_splitkv_plan -- the split count chosen for a device with `cus`
+ * compute units: 1 when B * H * ceil(N / 256) >= cus or N <= 448 (fewer than 8
+ * key tiles: the merge launch would cost more than the split saves), else
+ * ceil(cus / items) reduced to the largest useful count (see num_splits above).
+ * Pure function (no
+ * HIP call). Returns the count (>= 1) or a negative status for invalid shapes
+ * (FA_ERR_SHAPE, FA_ERR_HEADDIM, FA_ERR_ARG).
+ */
+int flash_attn_fwd_splitkv_plan(int64_t B, int64_t H, int64_t N, int64_t d, int causal, int cus);
+
+/*
+ * flash_attn_fwd_splitkv_workspace_size -- workspace bytes flash_attn_fwd_splitkv
+ * needs for num_splits (>= 1; reduced as above): S * B * H * N * (d + 1) * 4 for
+ * the resolved S > 1, and 0 when S resolves to 1 or the shape is empty. Negative
+ * status for invalid arguments. Pure function.
+ */
+int64_t flash_attn_fwd_splitkv_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, int causal,
+                                              int num_splits);
 
 /*
  * flash_attn_bwd -- gradients of the forward pass with respect to q, k and v.
@@ -141,7 +212,8 @@ int flash_attn_bwd_validate(const void* q, const void* k, const void* v, const v
 /* Static, never-freed description of a status code (unknown codes included). */
 const char* flash_attn_strerror(int status);
 
-/* ABI version of this header, currently 2 (1 had the forward pass only). */
+/* ABI version of this header, currently 3 (1: forward only; 2: + backward;
+ * 3: + key-split forward). */
 int flash_attn_abi_version(void);
 
 #ifdef __cplusplus

@@ -35,7 +35,8 @@ def test_library_loads_and_exports_header_symbols():
     assert os.path.exists(LIB_PATH), "build the library first (__graft_entry__.build())"
     names = _declared_functions()
     assert names == ["flash_attn_abi_version", "flash_attn_bwd", "flash_attn_bwd_validate", "flash_attn_fwd",
-                     "flash_attn_fwd_validate", "flash_attn_strerror"]
+                     "flash_attn_fwd_splitkv", "flash_attn_fwd_splitkv_plan", "flash_attn_fwd_splitkv_validate",
+                     "flash_attn_fwd_splitkv_workspace_size", "flash_attn_fwd_validate", "flash_attn_strerror"]
     lib = ctypes.CDLL(LIB_PATH)
     for n in names:
         assert hasattr(lib, n)
@@ -45,9 +46,10 @@ def test_library_loads_and_exports_header_symbols():
 
 
 def test_abi_version_and_strerror():
-    assert fa.flash_attn_abi_version() == 2
+    assert fa.flash_attn_abi_version() == 3
     codes = [fa.FA_OK, fa.FA_ERR_NULL, fa.FA_ERR_SHAPE, fa.FA_ERR_HEADDIM, fa.FA_ERR_DTYPE,
-             fa.FA_ERR_SCALE, fa.FA_ERR_ALIGN, fa.FA_ERR_ALIAS, fa.FA_ERR_HIP, fa.FA_ERR_ARG]
+             fa.FA_ERR_SCALE, fa.FA_ERR_ALIGN, fa.FA_ERR_ALIAS, fa.FA_ERR_HIP, fa.FA_ERR_ARG,
+             fa.FA_ERR_WORKSPACE]
     msgs = [fa.flash_attn_strerror(c) for c in codes]
     assert len(set(msgs)) == len(codes)
     assert fa.flash_attn_strerror(12345) == "unknown status"
@@ -186,3 +188,95 @@ def test_bwd_python_binding_rejects_bad_tensors():
         fa.backward(q, q, q, q, lse, q)                       # CPU tensors
     with pytest.raises(ValueError):
         fa.flash_attn_bwd(q, q, q, q, q, lse.double(), q, q, q, lse)   # lse dtype
+
+
+# ---- key-split forward ----
+
+def _sargs(q=A, k=A + GB, v=A + 2 * GB, o=A + 3 * GB, lse=A + 4 * GB, B=1, H=1, N=1024, d=64, causal=0,
+           scale=0.125, num_splits=4, ws=A + 5 * GB, ws_bytes=GB, stream=None, dtype=0):
+    return (q, k, v, o, lse, B, H, N, d, causal, scale, num_splits, ws, ws_bytes, stream, dtype)
+
+
+WS_1K = 4 * 1 * 1024 * 65 * 4   # workspace of B1 H1 N1024 d64 at 4 splits
+
+
+@pytest.mark.parametrize("B,H,N,d,causal,cus,want", [
+    (1, 1, 256, 64, 0, 256, 1),         # 1 item, but only 4 key tiles: too short to split
+    (1, 1, 448, 64, 0, 256, 1),         # 7 tiles: still too short
+    (1, 1, 512, 64, 0, 256, 8),         # 8 tiles: 8 ranges
+    (1, 1, 4096, 128, 0, 256, 16),      # 16 items want 16 ranges (the cap)
+    (1, 4, 4096, 128, 1, 256, 4),       # 64 items want 4; the first causal tile has 4 key tiles
+    (1, 1, 4096, 128, 1, 256, 4),       # wants 16, causal first tile allows 4
+    (1, 1, 100, 64, 1, 256, 1),         # 100 keys: 2 tiles, too short
+    (1, 1, 600, 64, 1, 256, 4),         # causal first query tile has 4 key tiles
+    (1, 1, 1, 64, 0, 256, 1),           # one key: nothing to split
+    (4, 16, 1024, 64, 0, 256, 1),       # 256 items fill 256 CUs
+    (2, 32, 4096, 128, 1, 256, 1),
+    (1, 8, 2048, 128, 0, 256, 4),       # 64 items -> 4
+    (1, 8, 2048, 128, 0, 304, 5),       # another CU count -> ceil(304 / 64) = 5
+    (1, 1, 4096, 128, 0, 0, 1),         # no device information: no split
+    (0, 4, 128, 64, 0, 256, 1),         # empty problem
+])
+def test_splitkv_plan(B, H, N, d, causal, cus, want):
+    assert fa.splitkv_plan(B, H, N, d, causal, cus) == want
+
+
+def test_splitkv_plan_and_size_reject_bad_shapes():
+    assert _native.splitkv_plan(-1, 1, 16, 64, 0, 256) == fa.FA_ERR_SHAPE
+    assert _native.splitkv_plan(1, 1, 16, 96, 0, 256) == fa.FA_ERR_HEADDIM
+    assert _native.splitkv_plan(1, 1, 16, 64, 3, 256) == fa.FA_ERR_ARG
+    assert _native.splitkv_workspace_size(1, 1, 16, 64, 0, 0) == fa.FA_ERR_ARG
+    assert _native.splitkv_workspace_size(1, -1, 16, 64, 0, 2) == fa.FA_ERR_SHAPE
+    assert _native.splitkv_workspace_size(1, 1, 16, 80, 0, 2) == fa.FA_ERR_HEADDIM
+
+
+@pytest.mark.parametrize("B,H,N,d,causal,splits,want", [
+    (1, 1, 1024, 64, 0, 4, WS_1K),
+    (1, 1, 1024, 64, 0, 1, 0),
+    (1, 1, 1024, 64, 0, 99, 16 * 1024 * 65 * 4),     # reduced to 16
+    (1, 1, 1024, 64, 1, 99, 4 * 1024 * 65 * 4),      # causal: reduced to 4
+    (2, 3, 100, 128, 0, 2, 2 * 6 * 100 * 129 * 4),
+    (2, 3, 100, 128, 0, 5, 2 * 6 * 100 * 129 * 4),   # 100 keys: 2 tiles
+    (1, 1, 0, 64, 0, 3, 0),
+])
+def test_splitkv_workspace_size(B, H, N, d, causal, splits, want):
+    assert fa.splitkv_workspace_size(B, H, N, d, causal, splits) == want
+
+
+BAD_SPLIT = [
+    (dict(num_splits=-1), fa.FA_ERR_ARG),
+    (dict(ws=None), fa.FA_ERR_WORKSPACE), (dict(ws=A + 5 * GB + 8), fa.FA_ERR_WORKSPACE),
+    (dict(ws_bytes=WS_1K - 1), fa.FA_ERR_WORKSPACE), (dict(ws_bytes=0), fa.FA_ERR_WORKSPACE),
+    (dict(ws=A), fa.FA_ERR_ALIAS), (dict(ws=A + 3 * GB - WS_1K + 16), fa.FA_ERR_ALIAS),
+    (dict(ws=A + 4 * GB), fa.FA_ERR_ALIAS),
+    # the forward's own checks still apply
+    (dict(d=96), fa.FA_ERR_HEADDIM), (dict(scale=0.0), fa.FA_ERR_SCALE), (dict(q=None), fa.FA_ERR_NULL),
+    (dict(o=A), fa.FA_ERR_ALIAS), (dict(causal=5), fa.FA_ERR_ARG), (dict(dtype=7), fa.FA_ERR_DTYPE),
+]
+
+
+@pytest.mark.parametrize("kw,code", BAD_SPLIT)
+def test_splitkv_validate_rejects(kw, code):
+    assert _native.validate_splitkv_raw(*_sargs(**kw)) == code
+
+
+@pytest.mark.parametrize("kw,code", BAD_SPLIT)
+def test_splitkv_rejects_before_launch(kw, code):
+    assert _native.splitkv_raw(*_sargs(**kw)) == code
+
+
+@pytest.mark.parametrize("kw", [
+    dict(), dict(ws_bytes=WS_1K), dict(ws=A + 4 * GB + 1024 * 4),        # just after lse
+    dict(num_splits=1, ws=None, ws_bytes=0),                             # resolves to the plain forward
+    dict(N=16, num_splits=8, ws=None, ws_bytes=0),                       # 16 keys: one tile, no split
+    dict(num_splits=0, ws=None, ws_bytes=0),                             # chosen at launch: not checked here
+    dict(causal=1, num_splits=50, ws_bytes=WS_1K),                       # reduced to 4
+])
+def test_splitkv_validate_accepts(kw):
+    assert _native.validate_splitkv_raw(*_sargs(**kw)) == fa.FA_OK
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0)])
+def test_splitkv_empty_problem_is_a_noop(kw):
+    assert _native.splitkv_raw(*_sargs(q=None, k=None, v=None, o=None, lse=None, ws=None, ws_bytes=0,
+                                       **kw)) == fa.FA_OK
