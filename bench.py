@@ -20,7 +20,10 @@ keeps the headline workload by default). --bwd times the backward pass instead
 dO), counted as 2.5x the forward's FLOPs (five N x N x d products instead of
 two), with the float64 backward oracle as its CPU baseline. --splitkv times the
 forward with and without the key split (flash_attn_fwd_splitkv, split count
-planned for this GPU) on the shapes that underfill it.
+planned for this GPU) on the shapes that underfill it. --strided times
+flash_attn_fwd_strided at the headline shape with head dimensions 80 and 96 and
+with q, k, v taken from one packed [B, N, 3, H, d] tensor (FLOPs counted with the
+real d).
 """
 from __future__ import annotations
 
@@ -281,6 +284,52 @@ def run_splitkv(args):
         print(json.dumps(line), flush=True)
 
 
+def run_strided(args):
+    """Diagnostic lines: the strided entry at the headline shape (B2 H32 N4096 causal bf16)."""
+    import torch
+
+    import exact_attention_flash_amd as fa
+    from exact_attention_flash_amd import inputs
+
+    dev = torch.device("cuda:0")
+    B, H, N = 2, 32, 4096
+    cases = [("contiguous d=128 (plain entry)", 128, False), ("contiguous d=80", 80, False),
+             ("contiguous d=96", 96, False), ("packed qkv [B,N,3,H,d] d=128, o [B,N,H,d]", 128, True)]
+    for label, d, packed in cases:
+        qb, kb, vb = inputs.draw_qkv((B, H, N, d), inputs.BF16, 1.0, 3)
+        q0, k0, v0 = (inputs.to_torch(x, inputs.BF16, dev) for x in (qb, kb, vb))
+        if packed:
+            pk = torch.stack([t.permute(0, 2, 1, 3) for t in (q0, k0, v0)], dim=2).contiguous()
+            q, k, v = (pk[:, :, i].permute(0, 2, 1, 3) for i in range(3))
+            o = torch.empty((B, N, H, d), dtype=torch.bfloat16, device=dev).permute(0, 2, 1, 3)
+        else:
+            q, k, v = q0, k0, v0
+            o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        scale = inputs.default_scale(d)
+        stream = torch.cuda.current_stream(dev)
+        if d == 128 and not packed:
+            step = lambda: fa.flash_attn_fwd(q, k, v, o, lse, causal=True, scale=scale, stream=stream)
+        else:
+            step = lambda: fa.flash_attn_fwd_strided(q, k, v, o, lse, causal=True, scale=scale, stream=stream)
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        flops = 4.0 * B * H * N * N * d / 2
+        print(json.dumps({"metric": "attention fwd TFLOP/s, strided entry (diagnostic)", "case": label,
+                          "config": {"B": B, "H": H, "N": N, "d": d, "causal": True, "dtype": "bf16"},
+                          "launch_ms": round(ms, 5), "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+                          "pct_of_bf16_peak": round(100 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                          "steps": args.steps, "warmup": args.warmup}), flush=True)
+
+
 def run(args, workload_name, causal):
     from exact_attention_flash_amd import inputs
 
@@ -338,6 +387,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-slices", type=int, default=64, help="(batch, head) slices the oracle times")
     ap.add_argument("--bwd", action="store_true", help="time the backward pass instead (diagnostic line)")
+    ap.add_argument("--strided", action="store_true",
+                    help="time the strided entry (head dims 80/96, packed qkv) at the headline shape (diagnostic)")
     ap.add_argument("--splitkv", action="store_true",
                     help="time the key-split forward against the plain one on underfilled shapes (diagnostic)")
     ap.add_argument("--cpu-bwd-slices", type=int, default=16,
@@ -362,6 +413,9 @@ def main():
 
     if args.splitkv:
         run_splitkv(args)
+        return
+    if args.strided:
+        run_strided(args)
         return
     runner = run_bwd if args.bwd else run
     if args.all:

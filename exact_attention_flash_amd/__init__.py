@@ -12,9 +12,10 @@ import math
 from . import _native
 from ._native import (FA_BF16, FA_FP16, FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEADDIM,  # noqa: F401
                       FA_ERR_DTYPE, FA_ERR_SCALE, FA_ERR_ALIGN, FA_ERR_ALIAS, FA_ERR_HIP, FA_ERR_ARG,
-                      FA_ERR_WORKSPACE)
+                      FA_ERR_WORKSPACE, FA_ERR_STRIDE)
 
-__all__ = ["forward", "backward", "forward_splitkv", "flash_attn_fwd", "flash_attn_fwd_splitkv", "flash_attn_bwd",
+__all__ = ["forward", "backward", "forward_splitkv", "flash_attn_fwd", "flash_attn_fwd_strided",
+           "flash_attn_fwd_splitkv", "flash_attn_bwd",
            "splitkv_plan", "splitkv_workspace_size", "flash_attn_strerror", "flash_attn_abi_version"]
 
 
@@ -69,14 +70,53 @@ def flash_attn_fwd(q, k, v, o, lse, causal: bool = False, scale: float | None = 
         raise FlashAttnError(st)
 
 
-def forward(q, k, v, causal: bool = False, scale: float | None = None, stream=None):
-    """Allocate O (q's dtype) and LSE (float32) and run the forward pass. Returns (o, lse)."""
+def flash_attn_fwd_strided(q, k, v, o, lse, causal: bool = False, scale: float | None = None,
+                           stream=None) -> None:
+    """The strided entry point on caller-owned [B, H, N, d] views (any strides with the
+    head dimension contiguous; d a multiple of 8 up to 128); lse [B, H, N] float32 with
+    contiguous rows."""
     import torch
 
-    B, H, N, _ = q.shape
-    o = torch.empty_like(q)
+    if q.dim() != 4:
+        raise ValueError("q must have shape [B, H, N, d]")
+    for name, t in (("k", k), ("v", v), ("o", o)):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{name} must match q in shape and dtype")
+    B, H, N, d = q.shape
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 with shape [B, H, N]")
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        if not t.is_cuda or t.device != q.device:
+            raise ValueError(f"{name} must be a GPU tensor on q's device")
+        if d > 1 and t.stride(3) != 1:
+            raise ValueError(f"{name}: the head dimension must be contiguous")
+    if not lse.is_cuda or lse.device != q.device or (N > 1 and lse.stride(2) != 1):
+        raise ValueError("lse must be a GPU tensor on q's device with contiguous rows")
+    dtype = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = _native.strided_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, d,
+                             q.stride()[:3], k.stride()[:3], v.stride()[:3], o.stride()[:3], lse.stride()[:2],
+                             causal, scale, stream.cuda_stream, dtype)
+    if st != FA_OK:
+        raise FlashAttnError(st, "flash_attn_fwd_strided")
+
+
+def forward(q, k, v, causal: bool = False, scale: float | None = None, stream=None):
+    """Allocate O (q's dtype, contiguous) and LSE (float32) and run the forward pass.
+    Returns (o, lse). Contiguous inputs with d of 64 or 128 take flash_attn_fwd; other
+    layouts and head dimensions take flash_attn_fwd_strided."""
+    import torch
+
+    B, H, N, d = q.shape
+    o = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    flash_attn_fwd(q, k, v, o, lse, causal=causal, scale=scale, stream=stream)
+    if d in (64, 128) and all(t.is_contiguous() for t in (q, k, v)):
+        flash_attn_fwd(q, k, v, o, lse, causal=causal, scale=scale, stream=stream)
+    else:
+        flash_attn_fwd_strided(q, k, v, o, lse, causal=causal, scale=scale, stream=stream)
     return o, lse
 
 

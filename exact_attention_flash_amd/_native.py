@@ -20,6 +20,7 @@ FA_ERR_ALIAS = -7
 FA_ERR_HIP = -8
 FA_ERR_ARG = -9
 FA_ERR_WORKSPACE = -10
+FA_ERR_STRIDE = -11
 
 _lib = None
 
@@ -41,6 +42,15 @@ def lib() -> ctypes.CDLL:
         ]
         L.flash_attn_fwd_validate.restype = ctypes.c_int
         L.flash_attn_fwd_validate.argtypes = L.flash_attn_fwd.argtypes
+        P64 = ctypes.POINTER(ctypes.c_int64)
+        L.flash_attn_fwd_strided.restype = ctypes.c_int
+        L.flash_attn_fwd_strided.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            P64, P64, P64, P64, P64, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_int,
+        ]
+        L.flash_attn_fwd_strided_validate.restype = ctypes.c_int
+        L.flash_attn_fwd_strided_validate.argtypes = L.flash_attn_fwd_strided.argtypes
         L.flash_attn_fwd_splitkv.restype = ctypes.c_int
         L.flash_attn_fwd_splitkv.argtypes = [
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -77,6 +87,28 @@ def fwd_raw(q, k, v, o, lse, B, H, N, d, causal, scale, stream, dtype) -> int:
 def validate_raw(q, k, v, o, lse, B, H, N, d, causal, scale, stream, dtype) -> int:
     """Call flash_attn_fwd_validate (host checks only, never launches)."""
     return lib().flash_attn_fwd_validate(q, k, v, o, lse, B, H, N, d, int(causal), float(scale), stream, dtype)
+
+
+def _strides(xs, n):
+    if xs is None:
+        return None
+    if len(xs) != n:
+        raise ValueError(f"expected {n} strides, got {len(xs)}")
+    return (ctypes.c_int64 * n)(*[int(x) for x in xs])
+
+
+def strided_raw(q, k, v, o, lse, B, H, N, d, qs, ks, vs, os_, ls, causal, scale, stream, dtype) -> int:
+    """Call flash_attn_fwd_strided (strides as sequences: 3 for q/k/v/o, 2 for lse; None -> NULL)."""
+    return lib().flash_attn_fwd_strided(q, k, v, o, lse, B, H, N, d, _strides(qs, 3), _strides(ks, 3),
+                                        _strides(vs, 3), _strides(os_, 3), _strides(ls, 2), int(causal),
+                                        float(scale), stream, dtype)
+
+
+def validate_strided_raw(q, k, v, o, lse, B, H, N, d, qs, ks, vs, os_, ls, causal, scale, stream, dtype) -> int:
+    """Call flash_attn_fwd_strided_validate (host checks only, never launches)."""
+    return lib().flash_attn_fwd_strided_validate(q, k, v, o, lse, B, H, N, d, _strides(qs, 3), _strides(ks, 3),
+                                                 _strides(vs, 3), _strides(os_, 3), _strides(ls, 2), int(causal),
+                                                 float(scale), stream, dtype)
 
 
 def splitkv_raw(q, k, v, o, lse, B, H, N, d, causal, scale, num_splits, ws, ws_bytes, stream, dtype) -> int:

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -22,7 +23,7 @@ bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p
 
 }  // namespace
 
-extern "C" int flash_attn_abi_version(void) { return 3; }
+extern "C" int flash_attn_abi_version(void) { return 4; }
 
 extern "C" const char* flash_attn_strerror(int status) {
   switch (status) {
@@ -37,6 +38,9 @@ extern "C" const char* flash_attn_strerror(int status) {
     case FA_ERR_HIP: return "HIP runtime error at launch";
     case FA_ERR_ARG: return "causal must be 0 or 1, and num_splits >= 0";
     case FA_ERR_WORKSPACE: return "workspace is NULL, misaligned or smaller than the split needs";
+    case FA_ERR_STRIDE:
+      return "a stride is negative, not a multiple of 8 elements, a row stride is below d or too large, a slice "
+             "spans 2 GiB or more, or an output overlaps itself";
     default: return "unknown status";
   }
 }
@@ -91,6 +95,123 @@ int check_args(const void* q, const void* k, const void* v, void* o, float* lse,
   a->splits = 1;
   a->part_o = nullptr;
   a->part_lse = nullptr;
+  // contiguous [B, H, N, d] layout
+  a->heads = static_cast<int>(H);
+  a->d_real = static_cast<int>(d);
+  a->q_sb = a->k_sb = a->v_sb = a->o_sb = H * N * d;
+  a->q_sh = a->k_sh = a->v_sh = a->o_sh = N * d;
+  a->q_sn = a->k_sn = a->v_sn = a->o_sn = static_cast<int>(d);
+  a->l_sb = H * N;
+  a->l_sh = N;
+  a->q_ext = a->k_ext = a->v_ext = static_cast<uint32_t>(N * d * 2);
+  return FA_OK;
+}
+
+// ---- strided layout ----
+
+// Offset (elements) one past the last element of a [B, H, N, inner] view whose
+// innermost dimension is contiguous; false if it does not fit comfortably in int64.
+bool view_end(int64_t B, int64_t H, int64_t N, int64_t inner, int64_t sb, int64_t sh, int64_t sn, int64_t* end) {
+  const __int128 e = static_cast<__int128>(B - 1) * sb + static_cast<__int128>(H - 1) * sh +
+                     static_cast<__int128>(N - 1) * sn + inner;
+  if (e > (static_cast<__int128>(1) << 60)) return false;
+  *end = static_cast<int64_t>(e);
+  return true;
+}
+
+// Sufficient condition for a view with a contiguous innermost dimension of `inner`
+// elements to address every element once: taken in increasing stride order, each
+// dimension of size > 1 steps past everything spanned by the dimensions inside it.
+bool no_self_overlap(int64_t inner, const int64_t (&size)[3], const int64_t (&stride)[3]) {
+  int idx[3] = {0, 1, 2};
+  std::sort(idx, idx + 3, [&](int x, int y) { return stride[x] < stride[y]; });
+  __int128 ext = inner;
+  for (int t = 0; t < 3; ++t) {
+    const int i = idx[t];
+    if (size[i] <= 1) continue;
+    if (stride[i] < ext) return false;
+    ext += static_cast<__int128>(size[i] - 1) * stride[i];
+  }
+  return true;
+}
+
+int check_strided(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                  int64_t N, int64_t d, const int64_t* qs, const int64_t* ks, const int64_t* vs, const int64_t* os,
+                  const int64_t* ls, int causal, float scale, int dtype, fa::FwdArgs* a, bool* empty) {
+  *empty = false;
+  if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
+  if (d < 8 || d > 128 || d % 8 != 0) return FA_ERR_HEADDIM;
+  if (dtype != FA_BF16 && dtype != FA_FP16) return FA_ERR_DTYPE;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
+  if (B == 0 || H == 0 || N == 0) {
+    *empty = true;
+    return FA_OK;
+  }
+  if (!qs || !ks || !vs || !os || !ls) return FA_ERR_NULL;
+  const int64_t rows = fa::rows_per_workgroup();
+  if (N > INT32_MAX / 2) return FA_ERR_SHAPE;
+  if (B > INT32_MAX / H) return FA_ERR_SHAPE;
+  const int64_t bh = B * H;
+  const int64_t q_tiles = (N + rows - 1) / rows;
+  if (bh > INT32_MAX / q_tiles) return FA_ERR_SHAPE;
+
+  // 16-bit tensors: strides >= 0 and multiples of 8 elements (16-byte row starts),
+  // row stride in [d, 2^23), one slice under 2 GiB
+  const int64_t* st16[4] = {qs, ks, vs, os};
+  for (const int64_t* t : st16) {
+    for (int i = 0; i < 3; ++i)
+      if (t[i] < 0 || t[i] % 8 != 0) return FA_ERR_STRIDE;
+    if (t[2] < d || t[2] >= (int64_t{1} << 23)) return FA_ERR_STRIDE;
+    if (((N - 1) * t[2] + d) * 2 >= (int64_t{1} << 31)) return FA_ERR_STRIDE;
+  }
+  if (ls[0] < 0 || ls[1] < 0) return FA_ERR_STRIDE;
+  const int64_t size3[3] = {B, H, N};
+  const int64_t o_str[3] = {os[0], os[1], os[2]};
+  if (!no_self_overlap(d, size3, o_str)) return FA_ERR_STRIDE;
+  const int64_t size2[3] = {B, H, 1};
+  const int64_t l_str[3] = {ls[0], ls[1], 0};
+  if (!no_self_overlap(N, size2, l_str)) return FA_ERR_STRIDE;
+
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return FA_ERR_ALIGN;
+  int64_t qe, ke, ve, oe, le;
+  if (!view_end(B, H, N, d, qs[0], qs[1], qs[2], &qe) || !view_end(B, H, N, d, ks[0], ks[1], ks[2], &ke) ||
+      !view_end(B, H, N, d, vs[0], vs[1], vs[2], &ve) || !view_end(B, H, N, d, os[0], os[1], os[2], &oe) ||
+      !view_end(B, H, 1, N, ls[0], ls[1], 0, &le))
+    return FA_ERR_SHAPE;
+  const uint64_t qb = qe * 2, kb = ke * 2, vb = ve * 2, ob = oe * 2, lb = le * 4;
+  if (overlaps(o, ob, q, qb) || overlaps(o, ob, k, kb) || overlaps(o, ob, v, vb) || overlaps(lse, lb, q, qb) ||
+      overlaps(lse, lb, k, kb) || overlaps(lse, lb, v, vb) || overlaps(o, ob, lse, lb))
+    return FA_ERR_ALIAS;
+
+  a->q = q;
+  a->k = k;
+  a->v = v;
+  a->o = o;
+  a->lse = lse;
+  a->bh = static_cast<int>(bh);
+  a->n = static_cast<int>(N);
+  a->q_tiles = static_cast<int>(q_tiles);
+  a->grid = static_cast<int>(bh * q_tiles);
+  // slices of one XCD share K/V through its L2 only when they are distinct heads of
+  // a contiguous layout; the grouping itself is valid for any layout
+  a->xcd_grouped = (bh % 8 == 0) ? 1 : 0;
+  a->scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634074);
+  a->splits = 1;
+  a->part_o = nullptr;
+  a->part_lse = nullptr;
+  a->heads = static_cast<int>(H);
+  a->d_real = static_cast<int>(d);
+  a->q_sb = qs[0]; a->q_sh = qs[1]; a->q_sn = static_cast<int>(qs[2]);
+  a->k_sb = ks[0]; a->k_sh = ks[1]; a->k_sn = static_cast<int>(ks[2]);
+  a->v_sb = vs[0]; a->v_sh = vs[1]; a->v_sn = static_cast<int>(vs[2]);
+  a->o_sb = os[0]; a->o_sh = os[1]; a->o_sn = static_cast<int>(os[2]);
+  a->l_sb = ls[0]; a->l_sh = ls[1];
+  a->q_ext = static_cast<uint32_t>(((N - 1) * qs[2] + d) * 2);
+  a->k_ext = static_cast<uint32_t>(((N - 1) * ks[2] + d) * 2);
+  a->v_ext = static_cast<uint32_t>(((N - 1) * vs[2] + d) * 2);
   return FA_OK;
 }
 
@@ -177,6 +298,32 @@ extern "C" int flash_attn_fwd(const void* q, const void* k, const void* v, void*
   if (st != FA_OK || empty) return st;
   const hipError_t err = fa::launch_fwd(a, dtype == FA_FP16, static_cast<int>(d), causal == 1,
                                         static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+extern "C" int flash_attn_fwd_strided_validate(const void* q, const void* k, const void* v, void* o, float* lse,
+                                               int64_t B, int64_t H, int64_t N, int64_t d, const int64_t* q_strides,
+                                               const int64_t* k_strides, const int64_t* v_strides,
+                                               const int64_t* o_strides, const int64_t* lse_strides, int causal,
+                                               float scale, void* /*stream*/, int dtype) {
+  fa::FwdArgs a;
+  bool empty;
+  return check_strided(q, k, v, o, lse, B, H, N, d, q_strides, k_strides, v_strides, o_strides, lse_strides, causal,
+                       scale, dtype, &a, &empty);
+}
+
+extern "C" int flash_attn_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                                      int64_t H, int64_t N, int64_t d, const int64_t* q_strides,
+                                      const int64_t* k_strides, const int64_t* v_strides, const int64_t* o_strides,
+                                      const int64_t* lse_strides, int causal, float scale, void* stream, int dtype) {
+  fa::FwdArgs a;
+  bool empty;
+  const int st = check_strided(q, k, v, o, lse, B, H, N, d, q_strides, k_strides, v_strides, o_strides,
+                               lse_strides, causal, scale, dtype, &a, &empty);
+  if (st != FA_OK || empty) return st;
+  const int inst = d <= 64 ? 64 : 128;
+  const hipError_t err =
+      fa::launch_fwd(a, dtype == FA_FP16, inst, causal == 1, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -24,6 +24,16 @@ struct FwdArgs {
   int splits;
   float* part_o;
   float* part_lse;
+  // layout: element (b, h, i, c) of q sits at q + b*q_sb + h*q_sh + i*q_sn + c
+  // (likewise k, v, o; lse at b*l_sb + h*l_sh + i), with bh = b * heads + h. Only
+  // columns c < d_real exist (the kernel instance's D >= d_real; columns past
+  // d_real read as zeros and are never stored). *_ext: bytes from a slice's first
+  // element to the end of its last row, ((n - 1) * row stride + d_real) * 2.
+  int heads;
+  int d_real;
+  int64_t q_sb, q_sh, k_sb, k_sh, v_sb, v_sh, o_sb, o_sh, l_sb, l_sh;
+  int q_sn, k_sn, v_sn, o_sn;
+  uint32_t q_ext, k_ext, v_ext;
 };
 
 // Query rows handled by one workgroup.

@@ -37,6 +37,12 @@
 //    blocks of 32 rows, so under a causal mask every SIMD has the same amount of
 //    work on the diagonal tiles and late diagonal tiles cost half an iteration.
 //  * Exponentials use exp2 with scale*log2(e) folded into one FMA per score.
+//  * Layout: q, k, v and o are addressed through (batch, head, row) strides with
+//    the head dimension contiguous. A head dimension d below the instance's D
+//    (64 or 128) is masked the way "6.1 FlashAttention V1 in detail", §8.3 masks
+//    BLOCK_D > D: chunks past d are loaded from an offset outside the buffer
+//    descriptor's range, which writes zeros into LDS, so they add nothing to the
+//    scores, and output columns past d are not stored.
 //  * Causal: tiles past the workgroup's last row are never loaded; waves skip the
 //    math of tiles entirely after their rows; only tiles on the diagonal or at the
 //    end of the sequence evaluate the mask.
@@ -85,6 +91,10 @@ constexpr int kAhead = kStages - 2;  // tiles in flight ahead of use
 
 // partial row sums above this send a bf16 tile back through the exact maximum
 constexpr float kBig = 0x1p64f;
+
+// load offset of a masked head-dimension chunk: past every descriptor's range (the
+// host keeps slice extents below 2^31 bytes), so the load writes zeros to LDS
+constexpr uint32_t kMaskedOffset = 0x80000000u;
 
 template <int D>
 struct Geo {
@@ -136,7 +146,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
   const int splits = SPLIT ? a.splits : 1;
   const int n_items = hpx * a.q_tiles * splits;
   const int N = a.n;
-  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  // slice base (elements) of item slice bh in a tensor with batch/head strides sb, sh
+  auto slice_off = [&](int bh, int64_t sb, int64_t sh) { return (int64_t)(bh / a.heads) * sb + (bh % a.heads) * sh; };
   const int tiles_all = (N + kBN - 1) / kBN;
   // r-th item of this workgroup, or -1 past the end of its list
   auto item_index = [&](int r) {
@@ -165,12 +176,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
   // ---- direct-to-LDS tile loads: this wave fills blocks wave + 8*i of K and of V ----
   // lane `lane` of block b lands at chunk position 64*b + lane = (row, physical chunk);
   // it fetches the logical chunk physical ^ swz(row) of that row.
-  uint32_t ld_off[G::blocksPerTile / kWaves];
+  uint32_t k_ld[G::blocksPerTile / kWaves], v_ld[G::blocksPerTile / kWaves];
 #pragma unroll
   for (int i = 0; i < G::blocksPerTile / kWaves; ++i) {
     const int p = 64 * (wave + kWaves * i) + lane;
-    const int row = p / G::chunksPerRow, phys = p % G::chunksPerRow;
-    ld_off[i] = (uint32_t)row * G::rowBytes + (uint32_t)((phys ^ G::swz(row)) * 16);
+    const int row = p / G::chunksPerRow, logical = (p % G::chunksPerRow) ^ G::swz(row);
+    const bool live = logical * 8 < a.d_real;
+    k_ld[i] = live ? (uint32_t)row * (uint32_t)(2 * a.k_sn) + (uint32_t)(logical * 16) : kMaskedOffset;
+    v_ld[i] = live ? (uint32_t)row * (uint32_t)(2 * a.v_sn) + (uint32_t)(logical * 16) : kMaskedOffset;
   }
   // The workgroup's key tiles form one stream over its items; tile g of the stream
   // lives in ring stage g % kStages. A cursor walks the stream kAhead tiles ahead
@@ -180,9 +193,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
   const uint16_t *c_k = nullptr, *c_v = nullptr;
   auto cursor_item = [&]() {
     if (c_j < 0) return;
-    const int64_t off = (int64_t)item_bh(c_j) * N * D;
-    c_k = reinterpret_cast<const uint16_t*>(a.k) + off;
-    c_v = reinterpret_cast<const uint16_t*>(a.v) + off;
+    c_k = reinterpret_cast<const uint16_t*>(a.k) + slice_off(item_bh(c_j), a.k_sb, a.k_sh);
+    c_v = reinterpret_cast<const uint16_t*>(a.v) + slice_off(item_bh(c_j), a.v_sb, a.v_sh);
     c_n = item_last(c_j);
     c_t = item_first(c_j);
   };
@@ -190,14 +202,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
   // issue the cursor's tile and advance; false once the stream is exhausted
   auto issue_next = [&]() {
     if (c_j < 0) return false;
-    const uint32_t skip = (uint32_t)c_t * kBN * G::rowBytes;
-    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(c_k + (int64_t)c_t * kBN * D, head_bytes - skip);
-    const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(c_v + (int64_t)c_t * kBN * D, head_bytes - skip);
+    const int64_t r0 = (int64_t)c_t * kBN;
+    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(c_k + r0 * a.k_sn, a.k_ext - (uint32_t)(r0 * a.k_sn * 2));
+    const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(c_v + r0 * a.v_sn, a.v_ext - (uint32_t)(r0 * a.v_sn * 2));
     char* st = smem + (c_g % kStages) * G::stageBytes;
 #pragma unroll
     for (int i = 0; i < G::blocksPerTile / kWaves; ++i) {
-      buffer_load16_lds(kr, ld_off[i], st + 1024 * (wave + kWaves * i));
-      buffer_load16_lds(vr, ld_off[i], st + G::tileBytes + 1024 * (wave + kWaves * i));
+      buffer_load16_lds(kr, k_ld[i], st + 1024 * (wave + kWaves * i));
+      buffer_load16_lds(vr, v_ld[i], st + G::tileBytes + 1024 * (wave + kWaves * i));
     }
     ++c_g;
     if (++c_t == c_n) {
@@ -215,16 +227,19 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
   auto issue_q = [&](int j) {
     const int q0 = item_q0(j);
     const __amdgpu_buffer_rsrc_t qr =
-        buffer_rsrc(reinterpret_cast<const uint16_t*>(a.q) + (int64_t)item_bh(j) * N * D + (int64_t)q0 * D,
-                    head_bytes - (uint32_t)q0 * G::rowBytes);
+        buffer_rsrc(reinterpret_cast<const uint16_t*>(a.q) + slice_off(item_bh(j), a.q_sb, a.q_sh) +
+                        (int64_t)q0 * a.q_sn,
+                    a.q_ext - (uint32_t)((int64_t)q0 * a.q_sn * 2));
     int lw = lane + 64 * wave;
     asm volatile("" : "+v"(lw));  // recomputed per call rather than kept live
 #pragma unroll
     for (int i = 0; i < G::qLoadsPerWave; ++i) {
       const int p = lw + 64 * kWaves * i;
-      const int row = p / G::chunksPerRow, phys = p % G::chunksPerRow;
-      buffer_load16_lds(qr, (uint32_t)row * G::rowBytes + (uint32_t)((phys ^ G::swz(row)) * 16),
-                        qsm + 1024 * (wave + kWaves * i));
+      const int row = p / G::chunksPerRow, logical = (p % G::chunksPerRow) ^ G::swz(row);
+      const uint32_t off = logical * 8 < a.d_real
+                               ? (uint32_t)row * (uint32_t)(2 * a.q_sn) + (uint32_t)(logical * 16)
+                               : kMaskedOffset;
+      buffer_load16_lds(qr, off, qsm + 1024 * (wave + kWaves * i));
     }
   };
   u32x4 qreg[D / 16];
@@ -491,16 +506,18 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
     }
     if (!SPLIT && qrow < N) {
       const float inv = 1.0f / l_tot;
-      uint16_t* og = reinterpret_cast<uint16_t*>(a.o) + (int64_t)bh * N * D + (int64_t)qrow * D;
+      uint16_t* og = reinterpret_cast<uint16_t*>(a.o) + slice_off(bh, a.o_sb, a.o_sh) + (int64_t)qrow * a.o_sn;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const u32x2 w = {pack2<FP16>(acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv),
                            pack2<FP16>(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv)};
-          *reinterpret_cast<u32x2*>(og + db * 32 + 8 * g + 4 * h) = w;
+          // columns come in fours and d_real is a multiple of 8
+          if (db * 32 + 8 * g + 4 * h < a.d_real) *reinterpret_cast<u32x2*>(og + db * 32 + 8 * g + 4 * h) = w;
         }
-      if (h == 0) a.lse[(int64_t)bh * N + qrow] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994530942f;
+      if (h == 0)
+        a.lse[slice_off(bh, a.l_sb, a.l_sh) + qrow] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994530942f;
     }
     if (next_j < 0) break;
     g0 += n_tiles;

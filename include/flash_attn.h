@@ -44,7 +44,10 @@ typedef enum {
   FA_ERR_ALIAS = -7,   /* an output overlaps an input or another output          */
   FA_ERR_HIP = -8,     /* the HIP runtime reported an error at launch             */
   FA_ERR_ARG = -9,     /* causal is not 0 or 1, or num_splits is negative        */
-  FA_ERR_WORKSPACE = -10 /* split workspace NULL, not 16-byte aligned or too small */
+  FA_ERR_WORKSPACE = -10, /* split workspace NULL, not 16-byte aligned or too small */
+  FA_ERR_STRIDE = -11  /* strided call: a stride negative, not a multiple of 8 elements, a row
+                          stride below d or >= 2^23, a slice spanning >= 2 GiB, or o / lse
+                          overlapping itself                                         */
 } fa_status;
 
 /*
@@ -90,6 +93,50 @@ int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* 
 int flash_attn_fwd_validate(const void* q, const void* k, const void* v, void* o, float* lse,
                             int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
                             void* stream, int dtype);
+
+/*
+ * flash_attn_fwd_strided -- flash_attn_fwd on strided views and any head dimension
+ * d that is a multiple of 8 up to 128. The tensors are addressed as in the
+ * strided kernel interface of "6.1 FlashAttention V1 in detail", §8.3 (a stride
+ * per batch, head and row for each of q, k, v, o; batch and head strides for the
+ * row statistics), and a head dimension that is not a power of two is handled as
+ * that section handles BLOCK_D > D: the kernel works on the next size it is built
+ * for (64 or 128) with the positions past d masked, so they add nothing to the
+ * scores and are never stored.
+ *
+ * Element (b, h, i, c) of q is q[b*q_strides[0] + h*q_strides[1] + i*q_strides[2] + c]
+ * (in elements of `dtype`; the head dimension is contiguous), likewise k, v and o;
+ * lse[b, h, i] is lse[b*lse_strides[0] + h*lse_strides[1] + i] (fp32 elements).
+ * q_strides, k_strides, v_strides, o_strides: host arrays of 3 int64 (batch, head,
+ * row); lse_strides: host array of 2 int64 (batch, head). Read during the call only.
+ * Every other argument and the result are as for flash_attn_fwd.
+ *
+ * Requirements (FA_ERR_STRIDE otherwise): all strides >= 0; the strides of q, k,
+ * v and o multiples of 8 elements (so every row starts 16-byte aligned); each row
+ * stride >= d and < 2^23; ((N - 1) * row stride + d) * 2 < 2^31 bytes per slice;
+ * o and lse must not overlap themselves (checked with a sufficient condition:
+ * in increasing stride order every dimension of size > 1 steps past the span of
+ * the dimensions inside it). Inputs may overlap each other and may repeat
+ * (stride 0 shares one K/V head among all heads, for example). d must be a
+ * multiple of 8 in [8, 128] (FA_ERR_HEADDIM). o and lse must not overlap any
+ * input's span (FA_ERR_ALIAS). Requires B * H * ceil(N / 256) < 2^31.
+ */
+int flash_attn_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int64_t B, int64_t H, int64_t N, int64_t d,
+                           const int64_t* q_strides, const int64_t* k_strides, const int64_t* v_strides,
+                           const int64_t* o_strides, const int64_t* lse_strides,
+                           int causal, float scale, void* stream, int dtype);
+
+/*
+ * flash_attn_fwd_strided_validate -- the checks of flash_attn_fwd_strided alone
+ * (same arguments, same status); launches nothing and makes no HIP call.
+ */
+int flash_attn_fwd_strided_validate(const void* q, const void* k, const void* v, void* o, float* lse,
+                                    int64_t B, int64_t H, int64_t N, int64_t d,
+                                    const int64_t* q_strides, const int64_t* k_strides,
+                                    const int64_t* v_strides, const int64_t* o_strides,
+                                    const int64_t* lse_strides, int causal, float scale,
+                                    void* stream, int dtype);
 
 /*
  * flash_attn_fwd_splitkv -- the forward pass with every query tile's keys cut
@@ -212,8 +259,8 @@ int flash_attn_bwd_validate(const void* q, const void* k, const void* v, const v
 /* Static, never-freed description of a status code (unknown codes included). */
 const char* flash_attn_strerror(int status);
 
-/* ABI version of this header, currently 3 (1: forward only; 2: + backward;
- * 3: + key-split forward). */
+/* ABI version of this header, currently 4 (1: forward only; 2: + backward;
+ * 3: + key-split forward; 4: + strided forward). */
 int flash_attn_abi_version(void);
 
 #ifdef __cplusplus

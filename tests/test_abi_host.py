@@ -36,7 +36,8 @@ def test_library_loads_and_exports_header_symbols():
     names = _declared_functions()
     assert names == ["flash_attn_abi_version", "flash_attn_bwd", "flash_attn_bwd_validate", "flash_attn_fwd",
                      "flash_attn_fwd_splitkv", "flash_attn_fwd_splitkv_plan", "flash_attn_fwd_splitkv_validate",
-                     "flash_attn_fwd_splitkv_workspace_size", "flash_attn_fwd_validate", "flash_attn_strerror"]
+                     "flash_attn_fwd_splitkv_workspace_size", "flash_attn_fwd_strided",
+                     "flash_attn_fwd_strided_validate", "flash_attn_fwd_validate", "flash_attn_strerror"]
     lib = ctypes.CDLL(LIB_PATH)
     for n in names:
         assert hasattr(lib, n)
@@ -46,10 +47,10 @@ def test_library_loads_and_exports_header_symbols():
 
 
 def test_abi_version_and_strerror():
-    assert fa.flash_attn_abi_version() == 3
+    assert fa.flash_attn_abi_version() == 4
     codes = [fa.FA_OK, fa.FA_ERR_NULL, fa.FA_ERR_SHAPE, fa.FA_ERR_HEADDIM, fa.FA_ERR_DTYPE,
              fa.FA_ERR_SCALE, fa.FA_ERR_ALIGN, fa.FA_ERR_ALIAS, fa.FA_ERR_HIP, fa.FA_ERR_ARG,
-             fa.FA_ERR_WORKSPACE]
+             fa.FA_ERR_WORKSPACE, fa.FA_ERR_STRIDE]
     msgs = [fa.flash_attn_strerror(c) for c in codes]
     assert len(set(msgs)) == len(codes)
     assert fa.flash_attn_strerror(12345) == "unknown status"
@@ -280,3 +281,70 @@ def test_splitkv_validate_accepts(kw):
 def test_splitkv_empty_problem_is_a_noop(kw):
     assert _native.splitkv_raw(*_sargs(q=None, k=None, v=None, o=None, lse=None, ws=None, ws_bytes=0,
                                        **kw)) == fa.FA_OK
+
+
+# ---- strided forward ----
+# B2 H3 N100 d80 views; contiguous strides unless overridden (elements)
+
+def _cstr(H=3, N=100, d=80):
+    return (H * N * d, N * d, d)
+
+
+def _targs(q=A, k=A + GB, v=A + 2 * GB, o=A + 3 * GB, lse=A + 4 * GB, B=2, H=3, N=100, d=80, qs="c", ks="c",
+           vs="c", os_="c", ls="c", causal=0, scale=0.1, stream=None, dtype=0):
+    c = _cstr(H, N, d)
+    pick = lambda x: c if x == "c" else x
+    return (q, k, v, o, lse, B, H, N, d, pick(qs), pick(ks), pick(vs), pick(os_), (H * N, N) if ls == "c" else ls,
+            causal, scale, stream, dtype)
+
+
+BAD_STRIDED = [
+    (dict(d=12), fa.FA_ERR_HEADDIM), (dict(d=0), fa.FA_ERR_HEADDIM), (dict(d=136), fa.FA_ERR_HEADDIM),
+    (dict(d=4), fa.FA_ERR_HEADDIM),
+    (dict(qs=(24000, 8000, 79)), fa.FA_ERR_STRIDE),          # row stride below d and not a multiple of 8
+    (dict(ks=(24000, 8000, 72)), fa.FA_ERR_STRIDE),          # row stride below d
+    (dict(vs=(24000, 8004, 80)), fa.FA_ERR_STRIDE),          # head stride not a multiple of 8
+    (dict(qs=(-24000, 8000, 80)), fa.FA_ERR_STRIDE),
+    (dict(os_=(24000, 8000, 1 << 23)), fa.FA_ERR_STRIDE),    # row stride too large
+    (dict(N=20000, qs=(0, 0, 65536)), fa.FA_ERR_STRIDE),     # slice spans >= 2 GiB
+    (dict(os_=(24000, 0, 80)), fa.FA_ERR_STRIDE),            # heads of o overlap
+    (dict(os_=(24000, 4000, 80)), fa.FA_ERR_STRIDE),         # o's head stride inside a head's rows
+    (dict(ls=(300, 50)), fa.FA_ERR_STRIDE),                  # lse heads overlap
+    (dict(ls=(-1, 100)), fa.FA_ERR_STRIDE),
+    (dict(qs=None), fa.FA_ERR_NULL), (dict(ls=None), fa.FA_ERR_NULL), (dict(o=None), fa.FA_ERR_NULL),
+    (dict(q=A + 8), fa.FA_ERR_ALIGN), (dict(lse=A + 4 * GB + 2), fa.FA_ERR_ALIGN),
+    (dict(o=A + 16), fa.FA_ERR_ALIAS),                       # o inside q's span
+    (dict(lse=A + 2 * GB + 4000), fa.FA_ERR_ALIAS),          # lse inside v's span
+    (dict(dtype=3), fa.FA_ERR_DTYPE), (dict(causal=2), fa.FA_ERR_ARG), (dict(scale=-1.0), fa.FA_ERR_SCALE),
+    (dict(B=-1), fa.FA_ERR_SHAPE),
+]
+
+
+@pytest.mark.parametrize("kw,code", BAD_STRIDED)
+def test_strided_validate_rejects(kw, code):
+    assert _native.validate_strided_raw(*_targs(**kw)) == code
+
+
+@pytest.mark.parametrize("kw,code", BAD_STRIDED)
+def test_strided_rejects_before_launch(kw, code):
+    assert _native.strided_raw(*_targs(**kw)) == code
+
+
+@pytest.mark.parametrize("kw", [
+    dict(), dict(d=8), dict(d=128), dict(d=64), dict(d=120),
+    dict(qs=(100 * 3 * 3 * 80, 80, 3 * 3 * 80), ks=(100 * 3 * 3 * 80, 80, 3 * 3 * 80)),   # packed qkv rows
+    dict(ks=(8000, 0, 80), vs=(8000, 0, 80)),                   # one K/V head shared by all heads
+    dict(ks=(0, 0, 80), vs=(0, 0, 80)),                         # one K/V slice shared by everything
+    dict(os_=(100 * 3 * 80, 80, 3 * 80)),                       # o as [B, N, H, d]
+    dict(os_=(3 * 100 * 96, 100 * 96, 96)),                     # padded o rows
+    dict(ls=(3 * 128, 128)), dict(ls=(1, 2), B=2, H=1, N=1),    # padded lse rows; tiny
+    dict(o=A + 16, q=A + 3 * GB),                               # swapped places, still disjoint
+])
+def test_strided_validate_accepts(kw):
+    assert _native.validate_strided_raw(*_targs(**kw)) == fa.FA_OK
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0)])
+def test_strided_empty_problem_is_a_noop(kw):
+    args = _targs(q=None, k=None, v=None, o=None, lse=None, qs=None, ks=None, vs=None, os_=None, ls=None, **kw)
+    assert _native.strided_raw(*args) == fa.FA_OK

@@ -1,0 +1,179 @@
+"""GPU parity of flash_attn_fwd_strided: strided views and head dimensions that are
+not 64 or 128, against the float64 oracle (tolerances of tests/_parity.py).
+
+* Head dimensions d in {8, 24, 40, 56, 72, 80, 96, 120} (multiples of 8, masked up to
+  the 64- or 128-wide kernel as "6.1 FlashAttention V1 in detail", §8.3 masks
+  BLOCK_D > D), both dtypes and masks, ragged N.
+* Layouts: q, k, v as views of one packed [B, N, 3, H, d] projection output; o written
+  into a [B, N, H, d] tensor; padded rows whose padding holds NaN (never read: a read
+  would poison the result); padded output rows and lse rows whose padding must keep
+  its sentinel; one K/V head shared by all heads (head stride 0).
+* The contiguous call through the strided entry equals flash_attn_fwd bitwise.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+from exact_attention_flash_amd import inputs
+from oracle.dense import attention as oracle_attention
+from tests._parity import assert_parity, metrics
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def fa():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import exact_attention_flash_amd as fa_mod
+
+    fa_mod._native.lib()
+    return fa_mod
+
+
+def _scale(d):
+    return float(np.float32(1.0 / math.sqrt(d)))
+
+
+def _tdtype(dtype):
+    return torch.bfloat16 if dtype == inputs.BF16 else torch.float16
+
+
+def _dev_from_bits(bits, dtype):
+    return inputs.to_torch(bits, dtype, torch.device("cuda:0"))
+
+
+def _o64(t, dtype):
+    return inputs.bits_to_f64(inputs.from_torch_bits(t.contiguous()), dtype)
+
+
+def _oracle(bits, dtype, causal, scale):
+    q, k, v = (inputs.bits_to_f64(x, dtype) for x in bits)
+    return oracle_attention(q, k, v, scale, causal=causal)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", [inputs.BF16, inputs.FP16])
+@pytest.mark.parametrize("d", [8, 24, 40, 56, 72, 80, 96, 120])
+def test_head_dims(fa, d, dtype, causal):
+    shape = (2, 2, 300, d)
+    scale = _scale(d)
+    bits = inputs.draw_qkv(shape, dtype, 1.0, 700 + d + (1 if causal else 0))
+    q, k, v = (_dev_from_bits(x, dtype) for x in bits)
+    o, lse = fa.forward(q, k, v, causal=causal, scale=scale)   # contiguous, d not 64/128: strided entry
+    torch.cuda.synchronize()
+    ro, rl = _oracle(bits, dtype, causal, scale)
+    m = metrics(_o64(o, dtype), lse.double().cpu().numpy(), ro, rl, dtype)
+    _log(f"strided d={d} {dtype} causal={causal}: {m}")
+    assert_parity(m, f"d={d} {dtype} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 80, 128])
+def test_packed_qkv_and_bnhd_output(fa, d, causal):
+    """q, k, v are views of one [B, N, 3, H, d] tensor; o is a [B, N, H, d] tensor."""
+    B, H, N, dtype = 2, 3, 517, inputs.BF16
+    scale = _scale(d)
+    bits = inputs.draw_qkv((B, H, N, d), dtype, 1.0, 800 + d + (1 if causal else 0))
+    q0, k0, v0 = (_dev_from_bits(x, dtype) for x in bits)
+    packed = torch.stack([t.permute(0, 2, 1, 3) for t in (q0, k0, v0)], dim=2).contiguous()   # [B, N, 3, H, d]
+    q, k, v = (packed[:, :, i].permute(0, 2, 1, 3) for i in range(3))                         # [B, H, N, d] views
+    assert not q.is_contiguous() and q.stride() == (N * 3 * H * d, d, 3 * H * d, 1)
+    o_bnhd = torch.empty((B, N, H, d), dtype=_tdtype(dtype), device="cuda:0")
+    o = o_bnhd.permute(0, 2, 1, 3)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda:0")
+    fa.flash_attn_fwd_strided(q, k, v, o, lse, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    ro, rl = _oracle(bits, dtype, causal, scale)
+    m = metrics(_o64(o, dtype), lse.double().cpu().numpy(), ro, rl, dtype)
+    _log(f"packed qkv d={d} causal={causal}: {m}")
+    assert_parity(m, f"packed d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("dtype", [inputs.BF16, inputs.FP16])
+@pytest.mark.parametrize("d", [40, 64, 96])
+def test_padding_is_never_read_or_written(fa, d, dtype):
+    """Inputs with row stride d + 24 whose padding holds NaN; o and lse with padded rows
+    holding a sentinel that must survive."""
+    B, H, N, pad = 1, 2, 333, 24
+    scale = _scale(d)
+    bits = inputs.draw_qkv((B, H, N, d), dtype, 1.0, 900 + d)
+    dev = torch.device("cuda:0")
+    views = []
+    for x in bits:
+        full = torch.full((B, H, N, d + pad), float("nan"), dtype=_tdtype(dtype), device=dev)
+        full[..., :d] = _dev_from_bits(x, dtype)
+        views.append(full[..., :d])
+    o_full = torch.full((B, H, N, d + pad), 7.0, dtype=_tdtype(dtype), device=dev)
+    lse_full = torch.full((B, H, N + 5), -3.0, dtype=torch.float32, device=dev)
+    o, lse = o_full[..., :d], lse_full[..., :N]
+    fa.flash_attn_fwd_strided(*views, o, lse, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    ro, rl = _oracle(bits, dtype, True, scale)
+    m = metrics(_o64(o, dtype), lse.double().cpu().numpy(), ro, rl, dtype)
+    assert_parity(m, f"padded d={d} {dtype}")
+    assert torch.all(o_full[..., d:] == 7.0).item(), "output padding was written"
+    assert torch.all(lse_full[..., N:] == -3.0).item(), "lse padding was written"
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_shared_kv_head(fa, causal):
+    """Head stride 0 for K and V: every query head attends the one K/V head."""
+    B, H, N, d, dtype = 2, 4, 260, 80, inputs.FP16
+    scale = _scale(d)
+    qb, _, _ = inputs.draw_qkv((B, H, N, d), dtype, 1.0, 950)
+    _, kb, vb = inputs.draw_qkv((B, 1, N, d), dtype, 1.0, 951)
+    q = _dev_from_bits(qb, dtype)
+    k1, v1 = _dev_from_bits(kb, dtype), _dev_from_bits(vb, dtype)
+    k, v = k1.expand(B, H, N, d), v1.expand(B, H, N, d)
+    assert k.stride(1) == 0
+    o = torch.empty((B, H, N, d), dtype=_tdtype(dtype), device="cuda:0")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda:0")
+    fa.flash_attn_fwd_strided(q, k, v, o, lse, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    kfull = np.broadcast_to(kb, (B, H, N, d))
+    vfull = np.broadcast_to(vb, (B, H, N, d))
+    ro, rl = _oracle((qb, kfull, vfull), dtype, causal, scale)
+    m = metrics(_o64(o, dtype), lse.double().cpu().numpy(), ro, rl, dtype)
+    assert_parity(m, f"shared kv causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_contiguous_strided_equals_plain(fa, d, causal):
+    shape, dtype = (2, 3, 400, d), inputs.BF16
+    bits = inputs.draw_qkv(shape, dtype, 1.0, 960 + d)
+    q, k, v = (_dev_from_bits(x, dtype) for x in bits)
+    o1, l1 = fa.forward(q, k, v, causal=causal, scale=0.1)
+    o2 = torch.empty_like(q)
+    l2 = torch.empty_like(l1)
+    fa.flash_attn_fwd_strided(q, k, v, o2, l2, causal=causal, scale=0.1)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_workload_shape_d80(fa):
+    """B2 H32 N4096 at d = 80 (a non-power-of-2 head dimension at the headline shape),
+    causal bf16; sampled heads against the oracle."""
+    B, H, N, d, dtype = 2, 32, 4096, 80, inputs.BF16
+    scale = _scale(d)
+    bits = inputs.draw_qkv((B, H, N, d), dtype, 1.0, 970)
+    q, k, v = (_dev_from_bits(x, dtype) for x in bits)
+    o, lse = fa.forward(q, k, v, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    heads = [0, 33, 63]
+    sel = lambda x: x.reshape(B * H, N, d)[heads]
+    ro, rl = _oracle(tuple(sel(x) for x in bits), dtype, True, scale)
+    og = _o64(o, dtype).reshape(B * H, N, d)[heads]
+    lg = lse.double().cpu().numpy().reshape(B * H, N)[heads]
+    m = metrics(og, lg, ro, rl, dtype)
+    _log(f"d=80 headline shape heads {heads}: {m}")
+    assert_parity(m, "d=80 headline shape")
