@@ -312,8 +312,17 @@ def run_strided(args):
             step = lambda: fa.flash_attn_fwd(q, k, v, o, lse, causal=True, scale=scale, stream=stream)
         else:
             step = lambda: fa.flash_attn_fwd_strided(q, k, v, o, lse, causal=True, scale=scale, stream=stream)
+        # same protocol as time_gpu: warm-up, one pass of per-launch events (this also
+        # brings the clocks back up after the idle time of drawing the inputs), then
+        # the timed back-to-back launches
         for _ in range(args.warmup):
             step()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for a_, b_ in evs:
+            a_.record(stream)
+            step()
+            b_.record(stream)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
