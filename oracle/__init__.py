@@ -24,6 +24,9 @@ Modules:
   ([V1] §6.1, [IO] "Backward Pass Recomputation").
 * ``splitkv`` -- attention over one key range (a block's O, m, l) and the merge
   of blocks with the two-block rule of [IO] "Online Softmax Mathematics".
+* ``fp8`` -- E4M3 encode/decode (OCP format), power-of-two block scales per 64
+  rows, block quantization, and exact attention on the dequantized inputs ([IO],
+  FlashAttention-3: FP8 with block-level quantization and dynamic scales).
 
 Every function is pinned by tests that do not re-type its formula: the worked
 example printed in [TL], closed forms, invariants, a brute-force fsum evaluation
