@@ -23,7 +23,9 @@ forward with and without the key split (flash_attn_fwd_splitkv, split count
 planned for this GPU) on the shapes that underfill it. --strided times
 flash_attn_fwd_strided at the headline shape with head dimensions 80 and 96 and
 with q, k, v taken from one packed [B, N, 3, H, d] tensor (FLOPs counted with the
-real d).
+real d). --fp8 times the FP8 path at the headline shape: flash_attn_fwd_fp8 alone
+(the attention on quantized inputs; FLOPs as the metric counts them, against the
+5 PFLOP/s dense FP8 peak) and the three quantization calls.
 """
 from __future__ import annotations
 
@@ -42,6 +44,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA, vendor figure
 PEAK_HBM_GBS = 8000.0
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense FP8 MFMA, vendor figure
 KERNEL_SOURCES = ["exact_attention_flash_amd/csrc/fwd_kernel.hip", "exact_attention_flash_amd/csrc/fwd_kernel.h",
                   "exact_attention_flash_amd/csrc/gfx950_ops.h"]
 BWD_FLOP_FACTOR = 2.5       # backward: S, dP, dV, dQ, dK products versus the forward's S and PV
@@ -339,6 +342,69 @@ def run_strided(args):
                           "steps": args.steps, "warmup": args.warmup}), flush=True)
 
 
+def _time_calls(step, steps, warmup, stream):
+    """time_gpu's protocol for an arbitrary step: warm-up, per-launch events, timed run."""
+    import torch
+
+    for _ in range(warmup):
+        step()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a_, b_ in evs:
+        a_.record(stream)
+        step()
+        b_.record(stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps, statistics.median(a_.elapsed_time(b_) for a_, b_ in evs)
+
+
+def run_fp8(args):
+    """Diagnostic line: the FP8 forward at the headline shape (B2 H32 N4096 d128 causal)."""
+    import torch
+
+    import exact_attention_flash_amd as fa
+    from exact_attention_flash_amd import inputs
+
+    w = inputs.WORKLOADS[inputs.HEADLINE]
+    dev = torch.device("cuda:0")
+    qb, kb, vb = inputs.workload_qkv(w)
+    q, k, v = (inputs.to_torch(x, w.dtype, dev) for x in (qb, kb, vb))
+    stream = torch.cuda.current_stream(dev)
+    scale = inputs.default_scale(w.d)
+    q8, qs = fa.quantize_fp8(q)
+    k8, ks = fa.quantize_fp8(k)
+    v8, vs = fa.quantize_fp8(v, keys_transposed=True)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    attn = lambda: fa.flash_attn_fwd_fp8(q8, k8, v8, qs, ks, vs, o, lse, causal=True, scale=scale, stream=stream)
+
+    def quant():
+        fa.quantize_fp8(q, stream=stream)
+        fa.quantize_fp8(k, stream=stream)
+        fa.quantize_fp8(v, keys_transposed=True, stream=stream)
+
+    ms, med = _time_calls(attn, args.steps, args.warmup, stream)
+    qms, _ = _time_calls(quant, max(10, args.steps // 4), args.warmup, stream)
+    flops = w.flops(True)
+    tf = flops / (ms * 1e-3) / 1e12
+    in_bytes = 3 * w.B * w.H * w.N * w.d * 2
+    print(json.dumps({
+        "metric": "attention fwd TFLOP/s on FP8 inputs (diagnostic)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": True,
+                   "inputs": "E4M3, power-of-two scale per 64 rows", "out_dtype": w.dtype},
+        "value": round(tf, 2), "unit": "TFLOP/s", "launch_ms": round(ms, 5), "launch_ms_median": round(med, 5),
+        "pct_of_fp8_peak": round(100 * tf / PEAK_FP8_TFLOPS, 2),
+        "pct_of_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+        "quantize_q_k_v_ms": round(qms, 5),
+        "quantize_GB_per_s": round((in_bytes + in_bytes / 2) / (qms * 1e-3) / 1e9, 1),
+        "steps": args.steps, "warmup": args.warmup}), flush=True)
+
+
 def run(args, workload_name, causal):
     from exact_attention_flash_amd import inputs
 
@@ -396,6 +462,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-slices", type=int, default=64, help="(batch, head) slices the oracle times")
     ap.add_argument("--bwd", action="store_true", help="time the backward pass instead (diagnostic line)")
+    ap.add_argument("--fp8", action="store_true",
+                    help="time the FP8 forward and the quantization at the headline shape (diagnostic)")
     ap.add_argument("--strided", action="store_true",
                     help="time the strided entry (head dims 80/96, packed qkv) at the headline shape (diagnostic)")
     ap.add_argument("--splitkv", action="store_true",
@@ -425,6 +493,9 @@ def main():
         return
     if args.strided:
         run_strided(args)
+        return
+    if args.fp8:
+        run_fp8(args)
         return
     runner = run_bwd if args.bwd else run
     if args.all:

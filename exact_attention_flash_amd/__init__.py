@@ -12,11 +12,12 @@ import math
 from . import _native
 from ._native import (FA_BF16, FA_FP16, FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEADDIM,  # noqa: F401
                       FA_ERR_DTYPE, FA_ERR_SCALE, FA_ERR_ALIGN, FA_ERR_ALIAS, FA_ERR_HIP, FA_ERR_ARG,
-                      FA_ERR_WORKSPACE, FA_ERR_STRIDE)
+                      FA_ERR_WORKSPACE, FA_ERR_STRIDE, FA_FP8_ROWS, FA_FP8_KEYS_T)
 
 __all__ = ["forward", "backward", "forward_splitkv", "flash_attn_fwd", "flash_attn_fwd_strided",
            "flash_attn_fwd_splitkv", "flash_attn_bwd",
-           "splitkv_plan", "splitkv_workspace_size", "flash_attn_strerror", "flash_attn_abi_version"]
+           "splitkv_plan", "splitkv_workspace_size", "quantize_fp8", "flash_attn_fwd_fp8", "forward_fp8",
+           "flash_attn_strerror", "flash_attn_abi_version"]
 
 
 class FlashAttnError(RuntimeError):
@@ -256,6 +257,69 @@ def backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = 
     delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     flash_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, causal=causal, scale=scale, stream=stream)
     return dq, dk, dv
+
+
+def quantize_fp8(x, keys_transposed: bool = False, stream=None):
+    """Block-quantize a contiguous [B, H, N, d] bf16/fp16 CUDA tensor to E4M3.
+
+    Returns (x8, scale_codes): x8 is uint8 [B, H, N, d] (rows layout) or
+    [B, H, ceil(N/64), d, 64] (keys-transposed layout, for values); scale_codes is
+    int32 [B, H, ceil(N/64)] holding e + 127 of each 64-row block's scale 2^e.
+    """
+    import torch
+
+    if x.dim() != 4 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [B, H, N, d] GPU tensor")
+    B, H, N, d = x.shape
+    t = -(-N // 64)
+    shape8 = (B, H, t, d, 64) if keys_transposed else (B, H, N, d)
+    x8 = torch.empty(shape8, dtype=torch.uint8, device=x.device)
+    se = torch.empty((B, H, t), dtype=torch.int32, device=x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    st = _native.quantize_raw(x.data_ptr(), x8.data_ptr(), se.data_ptr(), B, H, N, d,
+                              FA_FP8_KEYS_T if keys_transposed else FA_FP8_ROWS, stream.cuda_stream, _dtype_code(x))
+    if st != FA_OK:
+        raise FlashAttnError(st, "flash_attn_quantize_fp8")
+    return x8, se
+
+
+def flash_attn_fwd_fp8(q8, k8, v8t, q_scale, k_scale, v_scale, o, lse, causal: bool = False,
+                       scale: float | None = None, stream=None) -> None:
+    """The FP8 forward on caller-owned tensors (outputs of quantize_fp8; o [B, H, N, 128]
+    bf16/fp16 and lse [B, H, N] float32)."""
+    import torch
+
+    B, H, N, d = o.shape
+    for name, t in (("q8", q8), ("k8", k8), ("v8t", v8t), ("q_scale", q_scale), ("k_scale", k_scale),
+                    ("v_scale", v_scale), ("o", o), ("lse", lse)):
+        if not t.is_cuda or not t.is_contiguous() or t.device != o.device:
+            raise ValueError(f"{name} must be a contiguous GPU tensor on o's device")
+    if q8.shape != (B, H, N, d) or k8.shape != (B, H, N, d) or lse.shape != (B, H, N):
+        raise ValueError("shape mismatch among q8, k8, o, lse")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if stream is None:
+        stream = torch.cuda.current_stream(o.device)
+    st = _native.fp8_raw(q8.data_ptr(), k8.data_ptr(), v8t.data_ptr(), q_scale.data_ptr(), k_scale.data_ptr(),
+                         v_scale.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, d, causal, scale,
+                         stream.cuda_stream, _dtype_code(o))
+    if st != FA_OK:
+        raise FlashAttnError(st, "flash_attn_fwd_fp8")
+
+
+def forward_fp8(q, k, v, causal: bool = False, scale: float | None = None, stream=None):
+    """Quantize q, k, v to E4M3 (64-row blocks) and run the FP8 forward; o has q's dtype.
+    Returns (o, lse)."""
+    import torch
+
+    q8, qs = quantize_fp8(q, stream=stream)
+    k8, ks = quantize_fp8(k, stream=stream)
+    v8, vs = quantize_fp8(v, keys_transposed=True, stream=stream)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    flash_attn_fwd_fp8(q8, k8, v8, qs, ks, vs, o, lse, causal=causal, scale=scale, stream=stream)
+    return o, lse
 
 
 def flash_attn_strerror(status: int) -> str:

@@ -22,6 +22,9 @@ FA_ERR_ARG = -9
 FA_ERR_WORKSPACE = -10
 FA_ERR_STRIDE = -11
 
+FA_FP8_ROWS = 0
+FA_FP8_KEYS_T = 1
+
 _lib = None
 
 
@@ -51,6 +54,16 @@ def lib() -> ctypes.CDLL:
         ]
         L.flash_attn_fwd_strided_validate.restype = ctypes.c_int
         L.flash_attn_fwd_strided_validate.argtypes = L.flash_attn_fwd_strided.argtypes
+        vp = ctypes.c_void_p
+        L.flash_attn_quantize_fp8.restype = ctypes.c_int
+        L.flash_attn_quantize_fp8.argtypes = [vp, vp, vp] + [ctypes.c_int64] * 4 + [ctypes.c_int, vp, ctypes.c_int]
+        L.flash_attn_quantize_fp8_validate.restype = ctypes.c_int
+        L.flash_attn_quantize_fp8_validate.argtypes = L.flash_attn_quantize_fp8.argtypes
+        L.flash_attn_fwd_fp8.restype = ctypes.c_int
+        L.flash_attn_fwd_fp8.argtypes = [vp] * 8 + [ctypes.c_int64] * 4 + [ctypes.c_int, ctypes.c_float, vp,
+                                                                          ctypes.c_int]
+        L.flash_attn_fwd_fp8_validate.restype = ctypes.c_int
+        L.flash_attn_fwd_fp8_validate.argtypes = L.flash_attn_fwd_fp8.argtypes
         L.flash_attn_fwd_splitkv.restype = ctypes.c_int
         L.flash_attn_fwd_splitkv.argtypes = [
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -109,6 +122,24 @@ def validate_strided_raw(q, k, v, o, lse, B, H, N, d, qs, ks, vs, os_, ls, causa
     return lib().flash_attn_fwd_strided_validate(q, k, v, o, lse, B, H, N, d, _strides(qs, 3), _strides(ks, 3),
                                                  _strides(vs, 3), _strides(os_, 3), _strides(ls, 2), int(causal),
                                                  float(scale), stream, dtype)
+
+
+def quantize_raw(x, x8, se, B, H, N, d, layout, stream, dtype) -> int:
+    return lib().flash_attn_quantize_fp8(x, x8, se, B, H, N, d, int(layout), stream, dtype)
+
+
+def validate_quantize_raw(x, x8, se, B, H, N, d, layout, stream, dtype) -> int:
+    return lib().flash_attn_quantize_fp8_validate(x, x8, se, B, H, N, d, int(layout), stream, dtype)
+
+
+def fp8_raw(q8, k8, v8t, qs, ks, vs, o, lse, B, H, N, d, causal, scale, stream, out_dtype) -> int:
+    return lib().flash_attn_fwd_fp8(q8, k8, v8t, qs, ks, vs, o, lse, B, H, N, d, int(causal), float(scale), stream,
+                                    out_dtype)
+
+
+def validate_fp8_raw(q8, k8, v8t, qs, ks, vs, o, lse, B, H, N, d, causal, scale, stream, out_dtype) -> int:
+    return lib().flash_attn_fwd_fp8_validate(q8, k8, v8t, qs, ks, vs, o, lse, B, H, N, d, int(causal),
+                                             float(scale), stream, out_dtype)
 
 
 def splitkv_raw(q, k, v, o, lse, B, H, N, d, causal, scale, num_splits, ws, ws_bytes, stream, dtype) -> int:

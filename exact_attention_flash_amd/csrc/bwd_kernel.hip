@@ -48,13 +48,6 @@ constexpr int kAhead = 2;
 constexpr int kTile = 64;  // rows of a streamed tile (keys in bwd_dq, queries in bwd_dkdv)
 constexpr float kLog2e = 1.4426950408889634074f;
 
-// 4 bytes per lane from the buffer straight into LDS at lds_base + 4 * lane
-__device__ __forceinline__ void buffer_load4_lds(__amdgpu_buffer_rsrc_t r, uint32_t off, char* lds_base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)lds_base));
-  asm volatile("buffer_load_dword %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(m0) : "memory");
-}
-
 // Row-major 64-row tile of D-element rows in LDS (16-byte chunks swizzled by row).
 template <int D>
 struct Tile {

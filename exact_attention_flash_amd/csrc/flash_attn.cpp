@@ -10,6 +10,7 @@
 #include <cstdint>
 
 #include "bwd_kernel.h"
+#include "fp8_kernel.h"
 #include "fwd_kernel.h"
 
 namespace {
@@ -23,7 +24,7 @@ bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p
 
 }  // namespace
 
-extern "C" int flash_attn_abi_version(void) { return 4; }
+extern "C" int flash_attn_abi_version(void) { return 5; }
 
 extern "C" const char* flash_attn_strerror(int status) {
   switch (status) {
@@ -385,6 +386,129 @@ extern "C" int flash_attn_fwd_splitkv(const void* q, const void* k, const void* 
   if (st != FA_OK || empty) return st;
   const hipError_t err = fa::launch_fwd(a, dtype == FA_FP16, static_cast<int>(d), causal == 1,
                                         static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+// ---- FP8 ----
+
+namespace {
+
+int check_quant(const void* x, void* x8, int32_t* se, int64_t B, int64_t H, int64_t N, int64_t d, int layout,
+                int dtype, fa::QuantArgs* a, bool* empty) {
+  *empty = false;
+  if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (dtype != FA_BF16 && dtype != FA_FP16) return FA_ERR_DTYPE;
+  if (layout != FA_FP8_ROWS && layout != FA_FP8_KEYS_T) return FA_ERR_ARG;
+  if (B == 0 || H == 0 || N == 0) {
+    *empty = true;
+    return FA_OK;
+  }
+  if (N * d > INT32_MAX - 1 || B > INT32_MAX / H) return FA_ERR_SHAPE;
+  const int64_t bh = B * H, t64 = (N + fa::kFp8Block - 1) / fa::kFp8Block;
+  if (bh > INT32_MAX / t64) return FA_ERR_SHAPE;
+  if (!x || !x8 || !se) return FA_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(x8, 16) || !aligned(se, 4)) return FA_ERR_ALIGN;
+  const uint64_t xb = static_cast<uint64_t>(bh) * N * d * 2;
+  const uint64_t x8b = layout == FA_FP8_ROWS ? static_cast<uint64_t>(bh) * N * d
+                                             : static_cast<uint64_t>(bh) * t64 * d * fa::kFp8Block;
+  const uint64_t seb = static_cast<uint64_t>(bh) * t64 * 4;
+  if (overlaps(x8, x8b, x, xb) || overlaps(se, seb, x, xb) || overlaps(x8, x8b, se, seb)) return FA_ERR_ALIAS;
+  a->x = x;
+  a->x8 = static_cast<uint8_t*>(x8);
+  a->se = se;
+  a->bh = static_cast<int>(bh);
+  a->n = static_cast<int>(N);
+  a->t64 = static_cast<int>(t64);
+  return FA_OK;
+}
+
+int check_fp8(const void* q8, const void* k8, const void* v8t, const int32_t* qs, const int32_t* ks,
+              const int32_t* vs, void* o, float* lse, int64_t B, int64_t H, int64_t N, int64_t d, int causal,
+              float scale, int out_dtype, fa::Fp8Args* a, bool* empty) {
+  *empty = false;
+  if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
+  if (d != 128) return FA_ERR_HEADDIM;
+  if (out_dtype != FA_BF16 && out_dtype != FA_FP16) return FA_ERR_DTYPE;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
+  if (B == 0 || H == 0 || N == 0) {
+    *empty = true;
+    return FA_OK;
+  }
+  if (N * d > INT32_MAX - 1 || B > INT32_MAX / H) return FA_ERR_SHAPE;
+  const int64_t bh = B * H, t64 = (N + fa::kFp8Block - 1) / fa::kFp8Block;
+  const int64_t q_tiles = (N + fa::rows_per_workgroup() - 1) / fa::rows_per_workgroup();
+  if (bh > INT32_MAX / t64) return FA_ERR_SHAPE;
+  if (!q8 || !k8 || !v8t || !qs || !ks || !vs || !o || !lse) return FA_ERR_NULL;
+  if (!aligned(q8, 16) || !aligned(k8, 16) || !aligned(v8t, 16) || !aligned(o, 16) || !aligned(qs, 4) ||
+      !aligned(ks, 4) || !aligned(vs, 4) || !aligned(lse, 4))
+    return FA_ERR_ALIGN;
+  const uint64_t rb = static_cast<uint64_t>(bh) * N * d, vb = static_cast<uint64_t>(bh) * t64 * d * fa::kFp8Block;
+  const uint64_t sb = static_cast<uint64_t>(bh) * t64 * 4, ob = rb * 2, lb = static_cast<uint64_t>(bh) * N * 4;
+  const void* ins[6] = {q8, k8, v8t, qs, ks, vs};
+  const uint64_t inb[6] = {rb, rb, vb, sb, sb, sb};
+  for (int i = 0; i < 6; ++i)
+    if (overlaps(o, ob, ins[i], inb[i]) || overlaps(lse, lb, ins[i], inb[i])) return FA_ERR_ALIAS;
+  if (overlaps(o, ob, lse, lb)) return FA_ERR_ALIAS;
+  a->q8 = static_cast<const uint8_t*>(q8);
+  a->k8 = static_cast<const uint8_t*>(k8);
+  a->v8t = static_cast<const uint8_t*>(v8t);
+  a->q_se = qs;
+  a->k_se = ks;
+  a->v_se = vs;
+  a->o = o;
+  a->lse = lse;
+  a->bh = static_cast<int>(bh);
+  a->n = static_cast<int>(N);
+  a->t64 = static_cast<int>(t64);
+  a->q_tiles = static_cast<int>(q_tiles);
+  a->xcd_grouped = (bh % 8 == 0) ? 1 : 0;
+  a->scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634074);
+  a->e8m0_one = 127;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" int flash_attn_quantize_fp8_validate(const void* x, void* x8, int32_t* scale_codes, int64_t B, int64_t H,
+                                                int64_t N, int64_t d, int layout, void* /*stream*/, int dtype) {
+  fa::QuantArgs a;
+  bool empty;
+  return check_quant(x, x8, scale_codes, B, H, N, d, layout, dtype, &a, &empty);
+}
+
+extern "C" int flash_attn_quantize_fp8(const void* x, void* x8, int32_t* scale_codes, int64_t B, int64_t H,
+                                       int64_t N, int64_t d, int layout, void* stream, int dtype) {
+  fa::QuantArgs a;
+  bool empty;
+  const int st = check_quant(x, x8, scale_codes, B, H, N, d, layout, dtype, &a, &empty);
+  if (st != FA_OK || empty) return st;
+  const hipError_t err = fa::launch_quant_fp8(a, dtype == FA_FP16, static_cast<int>(d), layout == FA_FP8_KEYS_T,
+                                              static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+extern "C" int flash_attn_fwd_fp8_validate(const void* q8, const void* k8, const void* v8t, const int32_t* q_scale,
+                                           const int32_t* k_scale, const int32_t* v_scale, void* o, float* lse,
+                                           int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
+                                           void* /*stream*/, int out_dtype) {
+  fa::Fp8Args a;
+  bool empty;
+  return check_fp8(q8, k8, v8t, q_scale, k_scale, v_scale, o, lse, B, H, N, d, causal, scale, out_dtype, &a,
+                   &empty);
+}
+
+extern "C" int flash_attn_fwd_fp8(const void* q8, const void* k8, const void* v8t, const int32_t* q_scale,
+                                  const int32_t* k_scale, const int32_t* v_scale, void* o, float* lse, int64_t B,
+                                  int64_t H, int64_t N, int64_t d, int causal, float scale, void* stream,
+                                  int out_dtype) {
+  fa::Fp8Args a;
+  bool empty;
+  const int st = check_fp8(q8, k8, v8t, q_scale, k_scale, v_scale, o, lse, B, H, N, d, causal, scale, out_dtype,
+                           &a, &empty);
+  if (st != FA_OK || empty) return st;
+  const hipError_t err = fa::launch_fwd_fp8(a, out_dtype == FA_FP16, causal == 1, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -82,6 +82,14 @@ __device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, uint
   asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(m0) : "memory");
 }
 
+// 4 bytes per lane from the buffer straight into LDS at lds_base + 4 * lane
+// (buffer_load_dword ... lds); completion awaited with wait_vmcnt like the 16-byte form.
+__device__ __forceinline__ void buffer_load4_lds(__amdgpu_buffer_rsrc_t r, uint32_t off, char* lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)lds_base));
+  asm volatile("buffer_load_dword %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(m0) : "memory");
+}
+
 // s_waitcnt on the vector-memory counter only (gfx9 encoding: expcnt and lgkmcnt at max).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
