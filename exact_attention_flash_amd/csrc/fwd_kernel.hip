@@ -110,6 +110,17 @@ struct Geo {
   __device__ static __forceinline__ int swz(int row) { return chunk_swizzle<D>(row); }
 };
 
+// The kernel's argument block, read from the kernel-argument segment where a field
+// is used rather than kept in scalar registers for the whole kernel: the layout
+// fields read through it are needed only when a work item starts or ends, and the
+// scalar registers are needed by the tile loop.
+using KArgs = const __attribute__((address_space(4))) FwdArgs;
+__device__ __forceinline__ KArgs* kargs() {
+  KArgs* p = (KArgs*)(__builtin_amdgcn_kernarg_segment_ptr());
+  asm volatile("" : "+s"(p));
+  return p;
+}
+
 template <bool FP16, int D, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
   using G = Geo<D>;
@@ -147,7 +158,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
   const int n_items = hpx * a.q_tiles * splits;
   const int N = a.n;
   // slice base (elements) of item slice bh in a tensor with batch/head strides sb, sh
-  auto slice_off = [&](int bh, int64_t sb, int64_t sh) { return (int64_t)(bh / a.heads) * sb + (bh % a.heads) * sh; };
+  auto slice_off = [&](int bh, int64_t sb, int64_t sh) {
+    const int heads = kargs()->heads;
+    return (int64_t)(bh / heads) * sb + (bh % heads) * sh;
+  };
   const int tiles_all = (N + kBN - 1) / kBN;
   // r-th item of this workgroup, or -1 past the end of its list
   auto item_index = [&](int r) {
@@ -193,8 +207,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
   const uint16_t *c_k = nullptr, *c_v = nullptr;
   auto cursor_item = [&]() {
     if (c_j < 0) return;
-    c_k = reinterpret_cast<const uint16_t*>(a.k) + slice_off(item_bh(c_j), a.k_sb, a.k_sh);
-    c_v = reinterpret_cast<const uint16_t*>(a.v) + slice_off(item_bh(c_j), a.v_sb, a.v_sh);
+    KArgs* ka = kargs();
+    c_k = reinterpret_cast<const uint16_t*>(ka->k) + slice_off(item_bh(c_j), ka->k_sb, ka->k_sh);
+    c_v = reinterpret_cast<const uint16_t*>(ka->v) + slice_off(item_bh(c_j), ka->v_sb, ka->v_sh);
     c_n = item_last(c_j);
     c_t = item_first(c_j);
   };
@@ -203,8 +218,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
   auto issue_next = [&]() {
     if (c_j < 0) return false;
     const int64_t r0 = (int64_t)c_t * kBN;
-    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(c_k + r0 * a.k_sn, a.k_ext - (uint32_t)(r0 * a.k_sn * 2));
-    const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(c_v + r0 * a.v_sn, a.v_ext - (uint32_t)(r0 * a.v_sn * 2));
+    const __amdgpu_buffer_rsrc_t kr = uniform_rsrc(c_k + r0 * a.k_sn, a.k_ext - (uint32_t)(r0 * a.k_sn * 2));
+    const __amdgpu_buffer_rsrc_t vr = uniform_rsrc(c_v + r0 * a.v_sn, a.v_ext - (uint32_t)(r0 * a.v_sn * 2));
     char* st = smem + (c_g % kStages) * G::stageBytes;
 #pragma unroll
     for (int i = 0; i < G::blocksPerTile / kWaves; ++i) {
@@ -226,18 +241,21 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
   // item's Q is loaded while this item runs.
   auto issue_q = [&](int j) {
     const int q0 = item_q0(j);
+    KArgs* ka = kargs();
+    const int q_sn = ka->q_sn;
     const __amdgpu_buffer_rsrc_t qr =
-        buffer_rsrc(reinterpret_cast<const uint16_t*>(a.q) + slice_off(item_bh(j), a.q_sb, a.q_sh) +
-                        (int64_t)q0 * a.q_sn,
-                    a.q_ext - (uint32_t)((int64_t)q0 * a.q_sn * 2));
+        uniform_rsrc(reinterpret_cast<const uint16_t*>(ka->q) + slice_off(item_bh(j), ka->q_sb, ka->q_sh) +
+                        (int64_t)q0 * q_sn,
+                    ka->q_ext - (uint32_t)((int64_t)q0 * q_sn * 2));
+    const int d_real = ka->d_real;
     int lw = lane + 64 * wave;
     asm volatile("" : "+v"(lw));  // recomputed per call rather than kept live
 #pragma unroll
     for (int i = 0; i < G::qLoadsPerWave; ++i) {
       const int p = lw + 64 * kWaves * i;
       const int row = p / G::chunksPerRow, logical = (p % G::chunksPerRow) ^ G::swz(row);
-      const uint32_t off = logical * 8 < a.d_real
-                               ? (uint32_t)row * (uint32_t)(2 * a.q_sn) + (uint32_t)(logical * 16)
+      const uint32_t off = logical * 8 < d_real
+                               ? (uint32_t)row * (uint32_t)(2 * q_sn) + (uint32_t)(logical * 16)
                                : kMaskedOffset;
       buffer_load16_lds(qr, off, qsm + 1024 * (wave + kWaves * i));
     }
@@ -459,17 +477,24 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
     for (int i = 0; i <= n_tiles; ++i) {
       // one stream tile per iteration keeps the cursor kAhead tiles ahead; its stage
       // last held the tile kStages - kAhead before it, read before the last barrier
-      bool issued = false;
-      if (i < n_tiles) issued = issue_next();
+      // A wave stalls at a load instruction until the address unit takes it, and the
+      // unit takes about one 1 KiB block per 11-12 cycles per compute unit: with
+      // every wave issuing at the top of the iteration the last ones wait for
+      // hundreds of cycles. Group A issues at the top; group B issues after its
+      // softmax, when the queue has drained (tile first, then the next item's Q, so
+      // that the wait below can leave only Q in flight).
       const bool q_in_flight = i == 0 && next_j >= 0;
-      if (q_in_flight) issue_q(next_j);
       // A: matrix work of tile i, then its softmax; B: softmax of tile i-1, then
       // matrix work of tile i
       if (grp == 0) {
+        if (i < n_tiles) issue_next();
+        if (q_in_flight) issue_q(next_j);
         mfma_phase(i);
         softmax_phase(i);
       } else {
         softmax_phase(i - 1);
+        if (i < n_tiles) issue_next();
+        if (q_in_flight) issue_q(next_j);
         mfma_phase(i);
       }
       // tile i+1 must have landed (every wave waits for its own loads) before the
@@ -479,7 +504,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
         else wait_vmcnt<0>();
         __syncthreads();
       }
-      (void)issued;
     }
 
     // ---- epilogue: O = u / l, LSE = (m + log2 l) * ln 2 ----
@@ -493,7 +517,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
       const int64_t prow = ((int64_t)item_split(it_j) * a.bh + bh) * N + qrow;
       const bool live = l_tot > 0.f;
       const float inv = live ? 1.0f / l_tot : 0.f;
-      float* po = a.part_o + prow * D;
+      KArgs* ka = kargs();
+      float* po = ka->part_o + prow * D;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -502,11 +527,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
               f32x4{acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv, acc[db][4 * g + 2] * inv,
                     acc[db][4 * g + 3] * inv};
       if (h == 0)
-        a.part_lse[prow] = live ? (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994530942f : -INFINITY;
+        ka->part_lse[prow] = live ? (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994530942f : -INFINITY;
     }
     if (!SPLIT && qrow < N) {
       const float inv = 1.0f / l_tot;
-      uint16_t* og = reinterpret_cast<uint16_t*>(a.o) + slice_off(bh, a.o_sb, a.o_sh) + (int64_t)qrow * a.o_sn;
+      KArgs* ka = kargs();
+      const int d_real = ka->d_real;
+      uint16_t* og = reinterpret_cast<uint16_t*>(ka->o) + slice_off(bh, ka->o_sb, ka->o_sh) + (int64_t)qrow * ka->o_sn;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -514,10 +541,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
           const u32x2 w = {pack2<FP16>(acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv),
                            pack2<FP16>(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv)};
           // columns come in fours and d_real is a multiple of 8
-          if (db * 32 + 8 * g + 4 * h < a.d_real) *reinterpret_cast<u32x2*>(og + db * 32 + 8 * g + 4 * h) = w;
+          if (db * 32 + 8 * g + 4 * h < d_real) *reinterpret_cast<u32x2*>(og + db * 32 + 8 * g + 4 * h) = w;
         }
       if (h == 0)
-        a.lse[slice_off(bh, a.l_sb, a.l_sh) + qrow] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994530942f;
+        ka->lse[slice_off(bh, ka->l_sb, ka->l_sh) + qrow] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994530942f;
     }
     if (next_j < 0) break;
     g0 += n_tiles;
