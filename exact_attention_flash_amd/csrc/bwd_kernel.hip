@@ -80,6 +80,54 @@ struct Tile {
   }
 };
 
+// Products of the dK/dV kernel with the register file of each operand fixed. One
+// wave per SIMD holds K and V rows (B operands written once), the dK and dV
+// accumulators and a tile of S and dP: more than the 256 vector registers, so K,
+// V, dK and dV live in the accumulation registers (AGPRs), which MFMA reads and
+// writes directly, and S and dP, which the VALU works on, in vector registers.
+// The compiler's hazard checks do not see an MFMA inside an asm statement, so the
+// wait states they would insert are explicit: two before a product whose operand
+// the VALU may just have written (mfma32_aa), and mfma_drain() between the last
+// products and a VALU read of their results.
+// c (AGPR) += a (VGPR) b (VGPR), after two wait states
+template <bool FP16>
+__device__ __forceinline__ void mfma32_aa(u32x4 a, u32x4 b, f32x16& c) {
+  if constexpr (FP16)
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  else
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+// c (VGPR) = a (VGPR) b (AGPR), the first k-step of a product
+template <bool FP16>
+__device__ __forceinline__ f32x16 mfma32_va0(u32x4 a, u32x4 b) {
+  f32x16 c;
+  if constexpr (FP16)
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "a"(b));
+  else
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "a"(b));
+  return c;
+}
+// c (VGPR) += a (VGPR) b (AGPR)
+template <bool FP16>
+__device__ __forceinline__ void mfma32_va(u32x4 a, u32x4 b, f32x16& c) {
+  if constexpr (FP16)
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(b));
+  else
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(b));
+}
+// wait states between the last product and a read of its result (more than a
+// 32x32x16 product's latency); the results pass through the statement so that no
+// read of them is scheduled before it
+__device__ __forceinline__ void mfma_drain_v(f32x16 (&x)[2], f32x16 (&y)[2]) {
+  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" : "+v"(x[0]), "+v"(x[1]), "+v"(y[0]), "+v"(y[1]));
+}
+template <int N>
+__device__ __forceinline__ void mfma_drain_a(f32x16 (&x)[N], f32x16 (&y)[N]) {
+  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+a"(x[i]), "+a"(y[i]));
+}
+
 // B operand of k-step c (16 rows) from two 32x32 accumulators covering 64 rows:
 // elements 8 (c % 2) .. + 7 of accumulator c / 2, rounded to 16 bits
 template <bool FP16>
@@ -288,6 +336,7 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void bwd_dq(BwdArgs a) {
 // ------------------------------------------------------------------------------
 // 3. dK, dV: 4 waves x 32 keys, query tiles of 64 (Q, dO, L, D) streamed through LDS.
 constexpr int kKvWaves = 4;
+constexpr int kLookBwd = 3;  // LDS operand reads issued this many product steps ahead
 constexpr int kKvRows = 32 * kKvWaves;
 
 template <bool FP16, int D, bool CAUSAL>
@@ -390,6 +439,10 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv(BwdArgs a) {
   }
 
   for (int j = 0; j < n_tiles; ++j) {
+    // dK and dV stay in the accumulation registers across iterations (without this
+    // the loop-carried copy lands in vector registers and is copied every tile)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) asm volatile("" : "+a"(dk[db]), "+a"(dv[db]));
     if (j + kAhead < n_tiles) issue_tile(j + kAhead);
     const int qt0 = (t_first + j) * kTile;  // first query row of the tile
     // queries below this wave's first key see none of its keys (causal)
@@ -400,15 +453,33 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv(BwdArgs a) {
       const float* lt = reinterpret_cast<const float*>(qt + 2 * T::bytes);
       const float* dt = reinterpret_cast<const float*>(qt + 2 * T::bytes + kStat);
       // S = Q K^T and dP = dO V^T: two query blocks of 32, D/16 k-steps each
-      f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+      // operand reads from LDS are issued kLookBwd steps ahead of their products
+      f32x16 s[2], dp[2];
+      {
+        u32x4 qa[kLookBwd + 1], oa[kLookBwd + 1];
+        auto issue = [&](int st) {
+          const int kk = st >> 1, b = st & 1;
+          qa[st % (kLookBwd + 1)] = lds_read16(qt + r_off[kk] + b * 32 * T::rowBytes);
+          oa[st % (kLookBwd + 1)] = lds_read16(ot + r_off[kk] + b * 32 * T::rowBytes);
+        };
 #pragma unroll
-      for (int st = 0; st < D / 8; ++st) {
-        const int kk = st >> 1, b = st & 1;
-        const u32x4 qa = lds_read16(qt + r_off[kk] + b * 32 * T::rowBytes);
-        const u32x4 oa = lds_read16(ot + r_off[kk] + b * 32 * T::rowBytes);
-        s[b] = mfma32<FP16>(qa, kreg[kk], s[b]);
-        dp[b] = mfma32<FP16>(oa, vreg[kk], dp[b]);
+        for (int st = 0; st < kLookBwd; ++st) issue(st);
+#pragma unroll
+        for (int st = 0; st < D / 8; ++st) {
+          if (st + kLookBwd < D / 8) issue(st + kLookBwd);
+          __builtin_amdgcn_sched_barrier(0);
+          const int kk = st >> 1, b = st & 1, sl = st % (kLookBwd + 1);
+          if (kk == 0) {
+            s[b] = mfma32_va0<FP16>(qa[sl], kreg[kk]);
+            dp[b] = mfma32_va0<FP16>(oa[sl], vreg[kk]);
+          } else {
+            mfma32_va<FP16>(qa[sl], kreg[kk], s[b]);
+            mfma32_va<FP16>(oa[sl], vreg[kk], dp[b]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
+      mfma_drain_v(s, dp);
       // P and dS; query row = 32 b + 8 (r / 4) + 4 h + r % 4 within the tile
       const bool masked = CAUSAL && qt0 < key0 + 31;
 #pragma unroll
@@ -434,15 +505,26 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv(BwdArgs a) {
         dsb[t] = pack_b<FP16>(dp, t);
       }
       // dV^T += dO^T P and dK^T += Q^T dS
+      {
+        u32x2 olo[kLookBwd + 1], ohi[kLookBwd + 1], qlo[kLookBwd + 1], qhi[kLookBwd + 1];
+        auto issue = [&](int st) {
+          const int t = st / (D / 32), db = st % (D / 32), sl = st % (kLookBwd + 1);
+          olo[sl] = lds_read_tr16(ot + t_off[0][db] + 16 * t * T::rowBytes);
+          ohi[sl] = lds_read_tr16(ot + t_off[1][db] + 16 * t * T::rowBytes);
+          qlo[sl] = lds_read_tr16(qt + t_off[0][db] + 16 * t * T::rowBytes);
+          qhi[sl] = lds_read_tr16(qt + t_off[1][db] + 16 * t * T::rowBytes);
+        };
 #pragma unroll
-      for (int st = 0; st < D / 8; ++st) {
-        const int t = st / (D / 32), db = st % (D / 32);
-        const u32x2 olo = lds_read_tr16(ot + t_off[0][db] + 16 * t * T::rowBytes);
-        const u32x2 ohi = lds_read_tr16(ot + t_off[1][db] + 16 * t * T::rowBytes);
-        const u32x2 qlo = lds_read_tr16(qt + t_off[0][db] + 16 * t * T::rowBytes);
-        const u32x2 qhi = lds_read_tr16(qt + t_off[1][db] + 16 * t * T::rowBytes);
-        dv[db] = mfma32<FP16>(u32x4{olo[0], olo[1], ohi[0], ohi[1]}, pb[t], dv[db]);
-        dk[db] = mfma32<FP16>(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, dsb[t], dk[db]);
+        for (int st = 0; st < kLookBwd; ++st) issue(st);
+#pragma unroll
+        for (int st = 0; st < D / 8; ++st) {
+          if (st + kLookBwd < D / 8) issue(st + kLookBwd);
+          __builtin_amdgcn_sched_barrier(0);
+          const int t = st / (D / 32), db = st % (D / 32), sl = st % (kLookBwd + 1);
+          mfma32_aa<FP16>(u32x4{olo[sl][0], olo[sl][1], ohi[sl][0], ohi[sl][1]}, pb[t], dv[db]);
+          mfma32_aa<FP16>(u32x4{qlo[sl][0], qlo[sl][1], qhi[sl][0], qhi[sl][1]}, dsb[t], dk[db]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
     if (j + 1 < n_tiles) {
@@ -452,6 +534,7 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv(BwdArgs a) {
     }
   }
 
+  mfma_drain_a<D / 32>(dk, dv);
   if (key < N) {
     store_rows<FP16, D>(reinterpret_cast<uint16_t*>(a.dk) + head + (int64_t)key * D, dk, a.scale, h);
     store_rows<FP16, D>(reinterpret_cast<uint16_t*>(a.dv) + head + (int64_t)key * D, dv, 1.0f, h);
