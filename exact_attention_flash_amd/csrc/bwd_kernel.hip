@@ -121,6 +121,12 @@ __device__ __forceinline__ void mfma32_va(u32x4 a, u32x4 b, f32x16& c) {
 __device__ __forceinline__ void mfma_drain_v(f32x16 (&x)[2], f32x16 (&y)[2]) {
   asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" : "+v"(x[0]), "+v"(x[1]), "+v"(y[0]), "+v"(y[1]));
 }
+// wait states between a 32x32x16 product and a VALU access of its result, when at
+// least two more products were issued in between (the result passes through the
+// statement, so no access of it is scheduled before it)
+__device__ __forceinline__ void mfma_wait(f32x16& x, f32x16& y) {
+  asm volatile("s_nop 15\n\ts_nop 7" : "+v"(x), "+v"(y));
+}
 template <int N>
 __device__ __forceinline__ void mfma_drain_a(f32x16 (&x)[N], f32x16 (&y)[N]) {
   asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
@@ -386,24 +392,38 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv(BwdArgs a) {
   for (int i = 0; i < T::blocks / kKvWaves; ++i) ld_off[i] = T::src_offset(wave + kKvWaves * i, lane);
   // every wave loads the tile's L and D rows (the same bytes to the same place), so
   // that all waves issue the same number of loads per tile
-  auto issue_tile = [&](int j) {
+  // The kLoads loads of tile j, one at a time: load n < kLoads - 2 is Q block n / 2
+  // (even n) or dO block n / 2 (odd n) of this wave's share, then L and D.
+  struct TileSrc {
+    __amdgpu_buffer_rsrc_t q, o, l, d;
+    char* st;
+  };
+  auto tile_src = [&](int j) {
     const int t = t_first + j;
     const uint32_t skip = (uint32_t)t * kTile * T::rowBytes;
-    const __amdgpu_buffer_rsrc_t qr = buffer_rsrc(qg + (int64_t)t * kTile * D, head_bytes - skip);
-    const __amdgpu_buffer_rsrc_t orr = buffer_rsrc(og + (int64_t)t * kTile * D, head_bytes - skip);
     const uint32_t sskip = (uint32_t)t * kTile * 4;
-    const __amdgpu_buffer_rsrc_t lr = buffer_rsrc(lg + t * kTile, (uint32_t)N * 4 - sskip);
-    const __amdgpu_buffer_rsrc_t dr = buffer_rsrc(dg + t * kTile, (uint32_t)N * 4 - sskip);
-    char* st = smem + (j % kStages) * kStage;
-#pragma unroll
-    for (int i = 0; i < T::blocks / kKvWaves; ++i) {
-      buffer_load16_lds(qr, ld_off[i], st + 1024 * (wave + kKvWaves * i));
-      buffer_load16_lds(orr, ld_off[i], st + T::bytes + 1024 * (wave + kKvWaves * i));
-    }
-    buffer_load4_lds(lr, lane * 4, st + 2 * T::bytes);
-    buffer_load4_lds(dr, lane * 4, st + 2 * T::bytes + kStat);
+    return TileSrc{buffer_rsrc(qg + (int64_t)t * kTile * D, head_bytes - skip),
+                   buffer_rsrc(og + (int64_t)t * kTile * D, head_bytes - skip),
+                   buffer_rsrc(lg + t * kTile, (uint32_t)N * 4 - sskip),
+                   buffer_rsrc(dg + t * kTile, (uint32_t)N * 4 - sskip), smem + (j % kStages) * kStage};
   };
   constexpr int kLoads = 2 * T::blocks / kKvWaves + 2;
+  auto issue_load = [&](const TileSrc& ts, int n) {
+    if (n < kLoads - 2) {
+      const int i = n >> 1;
+      if ((n & 1) == 0) buffer_load16_lds(ts.q, ld_off[i], ts.st + 1024 * (wave + kKvWaves * i));
+      else buffer_load16_lds(ts.o, ld_off[i], ts.st + T::bytes + 1024 * (wave + kKvWaves * i));
+    } else if (n == kLoads - 2) {
+      buffer_load4_lds(ts.l, lane * 4, ts.st + 2 * T::bytes);
+    } else {
+      buffer_load4_lds(ts.d, lane * 4, ts.st + 2 * T::bytes + kStat);
+    }
+  };
+  auto issue_tile = [&](int j) {
+    const TileSrc ts = tile_src(j);
+#pragma unroll
+    for (int n = 0; n < kLoads; ++n) issue_load(ts, n);
+  };
 
   issue_tile(0);
   if (n_tiles > 1) issue_tile(1);
@@ -443,32 +463,80 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv(BwdArgs a) {
     // the loop-carried copy lands in vector registers and is copied every tile)
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) asm volatile("" : "+a"(dk[db]), "+a"(dv[db]));
-    if (j + kAhead < n_tiles) issue_tile(j + kAhead);
+    // tile j + kAhead: loaded one instruction per step of the dV/dK products (a
+    // load that waits for the address unit then holds up no product), or all at
+    // once here by a wave with no work in this tile
+    const bool load_next = j + kAhead < n_tiles;
     const int qt0 = (t_first + j) * kTile;  // first query row of the tile
     // queries below this wave's first key see none of its keys (causal)
     const bool active = key0 < N && (!CAUSAL || qt0 + kTile - 1 >= key0);
+    if (!active && load_next) issue_tile(j + kAhead);
     if (active) {
       const char* qt = smem + (j % kStages) * kStage;
       const char* ot = qt + T::bytes;
       const float* lt = reinterpret_cast<const float*>(qt + 2 * T::bytes);
       const float* dt = reinterpret_cast<const float*>(qt + 2 * T::bytes + kStat);
-      // S = Q K^T and dP = dO V^T: two query blocks of 32, D/16 k-steps each
-      // operand reads from LDS are issued kLookBwd steps ahead of their products
+      // The tile's 64 query rows form two blocks of 32. Products of block 0 run
+      // first; the VALU work of block 0 (P, dS and their 16-bit B operands) is
+      // interleaved with the S and dP products of block 1, and that of block 1
+      // with the dV and dK products of block 0, so that the exponentials run
+      // under matrix work instead of between its phases.
+      constexpr int kSd = D / 16;  // k-steps of one block's S (and dP) product
       f32x16 s[2], dp[2];
+      u32x4 pb[4], dsb[4];
+      // P and dS in place for query rows 32 b + 8 g + 4 h + r (r = 0..3)
+      const bool masked = CAUSAL && qt0 < key0 + 31;
+      auto p_ds = [&](int b, int g) {
+        const int row = 32 * b + 8 * g + 4 * h;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lt + row);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dt + row);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int e = 4 * g + r;
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][e], c, -l4[r] * kLog2e));
+          if (masked && qt0 + row + r < key) p = 0.f;
+          s[b][e] = p;
+          dp[b][e] = p * (dp[b][e] - d4[r]);
+        }
+      };
+      // VALU job j of block b: 0..3 P and dS of one row group, 4 and 5 the B operands
+      auto valu_job = [&](int b, int j) {
+        if (j < 4) {
+          p_ds(b, j);
+        } else if (j == 4) {
+          pb[2 * b] = pack_b<FP16>(s, 2 * b);
+          pb[2 * b + 1] = pack_b<FP16>(s, 2 * b + 1);
+        } else {
+          dsb[2 * b] = pack_b<FP16>(dp, 2 * b);
+          dsb[2 * b + 1] = pack_b<FP16>(dp, 2 * b + 1);
+        }
+      };
+      // the jobs of a block run after steps 1 .. kSd - 1 of the next product phase;
+      // the first reads accumulators that the products just before may still be
+      // writing: mfma_wait() supplies the wait states (the results pass through it,
+      // so no read is scheduled earlier)
+      auto jobs_after_step = [&](int b, int k) {
+        if (k == 1) mfma_wait(s[b], dp[b]);
+#pragma unroll
+        for (int jj = 0; jj < 6; ++jj)
+          if ((jj + 1 < kSd ? jj + 1 : kSd - 1) == k) valu_job(b, jj);
+      };
+      // S = Q K^T and dP = dO V^T, block 0 then block 1, D/16 k-steps each; operand
+      // reads from LDS are issued kLookBwd steps ahead of their products
       {
         u32x4 qa[kLookBwd + 1], oa[kLookBwd + 1];
         auto issue = [&](int st) {
-          const int kk = st >> 1, b = st & 1;
+          const int kk = st % kSd, b = st / kSd;
           qa[st % (kLookBwd + 1)] = lds_read16(qt + r_off[kk] + b * 32 * T::rowBytes);
           oa[st % (kLookBwd + 1)] = lds_read16(ot + r_off[kk] + b * 32 * T::rowBytes);
         };
 #pragma unroll
         for (int st = 0; st < kLookBwd; ++st) issue(st);
 #pragma unroll
-        for (int st = 0; st < D / 8; ++st) {
-          if (st + kLookBwd < D / 8) issue(st + kLookBwd);
+        for (int st = 0; st < 2 * kSd; ++st) {
+          if (st + kLookBwd < 2 * kSd) issue(st + kLookBwd);
           __builtin_amdgcn_sched_barrier(0);
-          const int kk = st >> 1, b = st & 1, sl = st % (kLookBwd + 1);
+          const int kk = st % kSd, b = st / kSd, sl = st % (kLookBwd + 1);
           if (kk == 0) {
             s[b] = mfma32_va0<FP16>(qa[sl], kreg[kk]);
             dp[b] = mfma32_va0<FP16>(oa[sl], vreg[kk]);
@@ -476,37 +544,16 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv(BwdArgs a) {
             mfma32_va<FP16>(qa[sl], kreg[kk], s[b]);
             mfma32_va<FP16>(oa[sl], vreg[kk], dp[b]);
           }
+          if (b == 1) jobs_after_step(0, kk);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      mfma_drain_v(s, dp);
-      // P and dS; query row = 32 b + 8 (r / 4) + 4 h + r % 4 within the tile
-      const bool masked = CAUSAL && qt0 < key0 + 31;
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int row = 32 * b + 8 * g + 4 * h;
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lt + row);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dt + row);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int e = 4 * g + r;
-            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][e], c, -l4[r] * kLog2e));
-            if (masked && qt0 + row + r < key) p = 0.f;
-            s[b][e] = p;
-            dp[b][e] = p * (dp[b][e] - d4[r]);
-          }
-        }
-      u32x4 pb[4], dsb[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        pb[t] = pack_b<FP16>(s, t);
-        dsb[t] = pack_b<FP16>(dp, t);
-      }
-      // dV^T += dO^T P and dK^T += Q^T dS
+      // dV^T += dO^T P and dK^T += Q^T dS: k-steps t = 0, 1 take block 0's rows
+      // (the first kSd steps), t = 2, 3 block 1's
       {
         u32x2 olo[kLookBwd + 1], ohi[kLookBwd + 1], qlo[kLookBwd + 1], qhi[kLookBwd + 1];
+        static_assert(kLoads <= D / 8, "one tile load per dV/dK step");
+        const TileSrc ts = tile_src(load_next ? j + kAhead : j);
         auto issue = [&](int st) {
           const int t = st / (D / 32), db = st % (D / 32), sl = st % (kLookBwd + 1);
           olo[sl] = lds_read_tr16(ot + t_off[0][db] + 16 * t * T::rowBytes);
@@ -523,6 +570,8 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv(BwdArgs a) {
           const int t = st / (D / 32), db = st % (D / 32), sl = st % (kLookBwd + 1);
           mfma32_aa<FP16>(u32x4{olo[sl][0], olo[sl][1], ohi[sl][0], ohi[sl][1]}, pb[t], dv[db]);
           mfma32_aa<FP16>(u32x4{qlo[sl][0], qlo[sl][1], qhi[sl][0], qhi[sl][1]}, dsb[t], dk[db]);
+          if (st < kLoads && load_next) issue_load(ts, st);
+          if (st < kSd) jobs_after_step(1, st);
           __builtin_amdgcn_sched_barrier(0);
         }
       }

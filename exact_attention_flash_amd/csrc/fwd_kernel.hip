@@ -529,22 +529,43 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
       if (h == 0)
         ka->part_lse[prow] = live ? (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994530942f : -INFINITY;
     }
-    if (!SPLIT && qrow < N) {
+    if (!SPLIT) {
+      // Rounded output in 16-byte pieces: a lane holds four columns of each group of
+      // eight and the lane 32 away the other four of the same row, so one swap of
+      // the two halves' words gives the lower half all eight columns of an even
+      // group and the upper half all eight of the odd group after it.
       const float inv = 1.0f / l_tot;
-      KArgs* ka = kargs();
-      const int d_real = ka->d_real;
-      uint16_t* og = reinterpret_cast<uint16_t*>(ka->o) + slice_off(bh, ka->o_sb, ka->o_sh) + (int64_t)qrow * ka->o_sn;
+      u32x4 w[D / 16];
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const u32x2 w = {pack2<FP16>(acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv),
-                           pack2<FP16>(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv)};
-          // columns come in fours and d_real is a multiple of 8
-          if (db * 32 + 8 * g + 4 * h < d_real) *reinterpret_cast<u32x2*>(og + db * 32 + 8 * g + 4 * h) = w;
+        for (int g = 0; g < 4; g += 2) {
+          const uint32_t e0 = pack2<FP16>(acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv);
+          const uint32_t e1 = pack2<FP16>(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
+          const uint32_t o0 = pack2<FP16>(acc[db][4 * g + 4] * inv, acc[db][4 * g + 5] * inv);
+          const uint32_t o1 = pack2<FP16>(acc[db][4 * g + 6] * inv, acc[db][4 * g + 7] * inv);
+          const auto s0 = __builtin_amdgcn_permlane32_swap(e0, o0, false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(e1, o1, false, false);
+          w[db * 2 + g / 2] = u32x4{s0[0], s1[0], s0[1], s1[1]};
         }
-      if (h == 0)
-        ka->lse[slice_off(bh, ka->l_sb, ka->l_sh) + qrow] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994530942f;
+      if (qrow < N) {
+        KArgs* ka = kargs();
+        const int d_real = ka->d_real;
+        uint16_t* og =
+            reinterpret_cast<uint16_t*>(ka->o) + slice_off(bh, ka->o_sb, ka->o_sh) + (int64_t)qrow * ka->o_sn + 8 * h;
+        if (d_real == D) {
+#pragma unroll
+          for (int k = 0; k < D / 16; ++k) *reinterpret_cast<u32x4*>(og + 16 * k) = w[k];
+        } else {
+          // d_real is a multiple of 8: each piece is wholly inside or outside
+#pragma unroll
+          for (int k = 0; k < D / 16; ++k)
+            if (16 * k + 8 * h < d_real) *reinterpret_cast<u32x4*>(og + 16 * k) = w[k];
+        }
+        if (h == 0)
+          ka->lse[slice_off(bh, ka->l_sb, ka->l_sh) + qrow] =
+              (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994530942f;
+      }
     }
     if (next_j < 0) break;
     g0 += n_tiles;
