@@ -203,7 +203,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
   // lives in ring stage g % kStages. A cursor walks the stream kAhead tiles ahead
   // of the matrix work, so the first tiles of the next item are in flight while the
   // current item finishes.
-  int c_r = 0, c_j = item_index(0), c_t = 0, c_n = 0, c_g = 0;
+  // (c_st: byte offset of the ring stage the cursor's tile goes to)
+  int c_r = 0, c_j = item_index(0), c_t = 0, c_n = 0, c_st = 0;
   const uint16_t *c_k = nullptr, *c_v = nullptr;
   auto cursor_item = [&]() {
     if (c_j < 0) return;
@@ -217,16 +218,18 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
   // issue the cursor's tile and advance; false once the stream is exhausted
   auto issue_next = [&]() {
     if (c_j < 0) return false;
-    const int64_t r0 = (int64_t)c_t * kBN;
-    const __amdgpu_buffer_rsrc_t kr = uniform_rsrc(c_k + r0 * a.k_sn, a.k_ext - (uint32_t)(r0 * a.k_sn * 2));
-    const __amdgpu_buffer_rsrc_t vr = uniform_rsrc(c_v + r0 * a.v_sn, a.v_ext - (uint32_t)(r0 * a.v_sn * 2));
-    char* st = smem + (c_g % kStages) * G::stageBytes;
+    // byte offsets of the tile in its slice (below the 32-bit extents)
+    const uint32_t k0 = (uint32_t)c_t * (uint32_t)(kBN * 2 * a.k_sn);
+    const uint32_t v0 = (uint32_t)c_t * (uint32_t)(kBN * 2 * a.v_sn);
+    const __amdgpu_buffer_rsrc_t kr = uniform_rsrc(reinterpret_cast<const char*>(c_k) + k0, a.k_ext - k0);
+    const __amdgpu_buffer_rsrc_t vr = uniform_rsrc(reinterpret_cast<const char*>(c_v) + v0, a.v_ext - v0);
+    char* st = smem + c_st;
 #pragma unroll
     for (int i = 0; i < G::blocksPerTile / kWaves; ++i) {
       buffer_load16_lds(kr, k_ld[i], st + 1024 * (wave + kWaves * i));
       buffer_load16_lds(vr, v_ld[i], st + G::tileBytes + 1024 * (wave + kWaves * i));
     }
-    ++c_g;
+    c_st = c_st + G::stageBytes == kStages * G::stageBytes ? 0 : c_st + G::stageBytes;
     if (++c_t == c_n) {
       c_j = item_index(++c_r);
       cursor_item();
