@@ -87,17 +87,17 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
 // possibly aliasing the in-flight copy (it would then wait for all outstanding
 // loads, tiles prefetched for later iterations included); completion is instead
 // awaited explicitly with wait_vmcnt before the barrier that publishes a tile.
+// M0 takes the LDS byte address, the low 32 bits of a generic pointer into LDS
+// (the cast to the LDS address space would add a null-pointer select).
 __device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, uint32_t off, char* lds_base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)lds_base));
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
   asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(m0) : "memory");
 }
 
 // 4 bytes per lane from the buffer straight into LDS at lds_base + 4 * lane
 // (buffer_load_dword ... lds); completion awaited with wait_vmcnt like the 16-byte form.
 __device__ __forceinline__ void buffer_load4_lds(__amdgpu_buffer_rsrc_t r, uint32_t off, char* lds_base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)lds_base));
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
   asm volatile("buffer_load_dword %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(m0) : "memory");
 }
 
