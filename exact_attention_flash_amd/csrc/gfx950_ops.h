@@ -88,17 +88,24 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
 // loads, tiles prefetched for later iterations included); completion is instead
 // awaited explicitly with wait_vmcnt before the barrier that publishes a tile.
 // M0 takes the LDS byte address, the low 32 bits of a generic pointer into LDS
-// (the cast to the LDS address space would add a null-pointer select).
+// (the cast to the LDS address space would add a null-pointer select). The load
+// reads scalar registers that the VALU may have just written: the descriptor and
+// M0 come from v_readfirstlane. A vector-memory instruction needs five wait states
+// after a VALU write of an SGPR it reads (and one after a write of M0); the
+// compiler inserts them for its own loads (s_nop 2 after a readfirstlane-built
+// descriptor and two other instructions) but cannot see the reads inside this asm,
+// so the s_nop 4 supplies all five. Without it, a wave issuing eight of these loads
+// in a row fetched wrong data for some of them.
 __device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, uint32_t off, char* lds_base) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(m0) : "memory");
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(m0) : "memory");
 }
 
 // 4 bytes per lane from the buffer straight into LDS at lds_base + 4 * lane
 // (buffer_load_dword ... lds); completion awaited with wait_vmcnt like the 16-byte form.
 __device__ __forceinline__ void buffer_load4_lds(__amdgpu_buffer_rsrc_t r, uint32_t off, char* lds_base) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
-  asm volatile("buffer_load_dword %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(m0) : "memory");
+  asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(m0) : "memory");
 }
 
 // s_waitcnt on the vector-memory counter only (gfx9 encoding: expcnt and lgkmcnt at max).
