@@ -87,8 +87,8 @@ struct Tile {
 // writes directly, and S and dP, which the VALU works on, in vector registers.
 // The compiler's hazard checks do not see an MFMA inside an asm statement, so the
 // wait states they would insert are explicit: two before a product whose operand
-// the VALU may just have written (mfma32_aa), and mfma_drain() between the last
-// products and a VALU read of their results.
+// the VALU may just have written (mfma32_aa), mfma_wait() before the first VALU
+// access of an S or dP block, and mfma_drain_a() before the accumulators are read.
 // c (AGPR) += a (VGPR) b (VGPR), after two wait states
 template <bool FP16>
 __device__ __forceinline__ void mfma32_aa(u32x4 a, u32x4 b, f32x16& c) {
@@ -114,12 +114,6 @@ __device__ __forceinline__ void mfma32_va(u32x4 a, u32x4 b, f32x16& c) {
     asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(b));
   else
     asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(b));
-}
-// wait states between the last product and a read of its result (more than a
-// 32x32x16 product's latency); the results pass through the statement so that no
-// read of them is scheduled before it
-__device__ __forceinline__ void mfma_drain_v(f32x16 (&x)[2], f32x16 (&y)[2]) {
-  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" : "+v"(x[0]), "+v"(x[1]), "+v"(y[0]), "+v"(y[1]));
 }
 // wait states between a 32x32x16 product and a VALU access of its result, when at
 // least two more products were issued in between (the result passes through the

@@ -104,7 +104,6 @@ struct Geo {
   static constexpr int stageBytes = 2 * tileBytes;  // K then V
   static constexpr int qBytes = kBM * rowBytes;       // the Q rows of one item
   static constexpr int blocksPerTile = tileBytes / 1024;  // 1 KiB per wave-instruction
-  static constexpr int loadsPerWave = 2 * blocksPerTile / kWaves;  // K + V instructions per wave per tile
   static constexpr int qLoadsPerWave = qBytes / 1024 / kWaves;       // Q instructions per wave per item
   static_assert(blocksPerTile % kWaves == 0, "tile must split into whole 1 KiB blocks per wave");
   __device__ static __forceinline__ int swz(int row) { return chunk_swizzle<D>(row); }
