@@ -489,13 +489,18 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
       const bool q_in_flight = i == 0 && next_j >= 0;
       // A: matrix work of tile i, then its softmax; B: softmax of tile i-1, then
       // matrix work of tile i
+      // (the raised issue priority of the matrix phase starts before the loads, so
+      // that the cursor work of the wave about to feed the matrix pipe is not held
+      // up by the other wave's softmax)
       if (grp == 0) {
+        __builtin_amdgcn_s_setprio(1);
         if (i < n_tiles) issue_next();
         if (q_in_flight) issue_q(next_j);
         mfma_phase(i);
         softmax_phase(i);
       } else {
         softmax_phase(i - 1);
+        __builtin_amdgcn_s_setprio(1);
         if (i < n_tiles) issue_next();
         if (q_in_flight) issue_q(next_j);
         mfma_phase(i);
