@@ -16,6 +16,7 @@ LIB_NAME = "libflash_attn_mi355x.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 SOURCES = [
     os.path.join(PKG_DIR, "csrc", "fwd_kernel.hip"),
+    os.path.join(PKG_DIR, "csrc", "fwd_sp.hip"),
     os.path.join(PKG_DIR, "csrc", "bwd_kernel.hip"),
     os.path.join(PKG_DIR, "csrc", "fp8_quant.hip"),
     os.path.join(PKG_DIR, "csrc", "fwd_fp8.hip"),

@@ -8,6 +8,8 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
+#include <cstring>
 
 #include "bwd_kernel.h"
 #include "fp8_kernel.h"
@@ -21,6 +23,18 @@ bool overlaps(const void* a, uint64_t an, const void* b, uint64_t bn) {
 }
 
 bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+// Forward kernel of a call without a key split: the software-pipelined kernel, or
+// the ping-pong kernel when FLASH_ATTN_FWD_KERNEL=pingpong (read once per process;
+// kept for comparisons). Calls with a key split always use the ping-pong kernel's
+// split instance.
+hipError_t launch_unsplit(const fa::FwdArgs& a, bool fp16, int d, bool causal, hipStream_t stream) {
+  static const bool pingpong = [] {
+    const char* e = std::getenv("FLASH_ATTN_FWD_KERNEL");
+    return e != nullptr && std::strcmp(e, "pingpong") == 0;
+  }();
+  return pingpong ? fa::launch_fwd(a, fp16, d, causal, stream) : fa::launch_fwd_sp(a, fp16, d, causal, stream);
+}
 
 }  // namespace
 
@@ -297,7 +311,7 @@ extern "C" int flash_attn_fwd(const void* q, const void* k, const void* v, void*
   bool empty;
   const int st = check_args(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, &a, &empty);
   if (st != FA_OK || empty) return st;
-  const hipError_t err = fa::launch_fwd(a, dtype == FA_FP16, static_cast<int>(d), causal == 1,
+  const hipError_t err = launch_unsplit(a, dtype == FA_FP16, static_cast<int>(d), causal == 1,
                                         static_cast<hipStream_t>(stream));
   return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -324,7 +338,7 @@ extern "C" int flash_attn_fwd_strided(const void* q, const void* k, const void* 
   if (st != FA_OK || empty) return st;
   const int inst = d <= 64 ? 64 : 128;
   const hipError_t err =
-      fa::launch_fwd(a, dtype == FA_FP16, inst, causal == 1, static_cast<hipStream_t>(stream));
+      launch_unsplit(a, dtype == FA_FP16, inst, causal == 1, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -384,8 +398,11 @@ extern "C" int flash_attn_fwd_splitkv(const void* q, const void* k, const void* 
   const int st = splitkv_common(q, k, v, o, lse, B, H, N, d, causal, scale, num_splits, workspace,
                                 workspace_bytes, dtype, true, &a, &empty);
   if (st != FA_OK || empty) return st;
-  const hipError_t err = fa::launch_fwd(a, dtype == FA_FP16, static_cast<int>(d), causal == 1,
-                                        static_cast<hipStream_t>(stream));
+  const hipError_t err =
+      a.splits > 1 ? fa::launch_fwd(a, dtype == FA_FP16, static_cast<int>(d), causal == 1,
+                                    static_cast<hipStream_t>(stream))
+                   : launch_unsplit(a, dtype == FA_FP16, static_cast<int>(d), causal == 1,
+                                    static_cast<hipStream_t>(stream));
   return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

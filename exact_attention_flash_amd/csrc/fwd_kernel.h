@@ -50,4 +50,8 @@ int device_cus();
 // split instance runs and is followed by the merge kernel.
 hipError_t launch_fwd(const FwdArgs& a, bool fp16, int d, bool causal, hipStream_t stream);
 
+// Enqueue the software-pipelined forward (no key split: a.splits must be 1) for
+// (dtype, d, causal); d is 64 or 128. Sizes the persistent grid like launch_fwd.
+hipError_t launch_fwd_sp(const FwdArgs& a, bool fp16, int d, bool causal, hipStream_t stream);
+
 }  // namespace fa

@@ -171,7 +171,7 @@ def _hazards(asm: str, kernel: str):
 
 @pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
                     reason="hipcc not available")
-@pytest.mark.parametrize("source", ["fwd_kernel.hip", "bwd_kernel.hip", "fwd_fp8.hip"])
+@pytest.mark.parametrize("source", ["fwd_kernel.hip", "fwd_sp.hip", "bwd_kernel.hip", "fwd_fp8.hip"])
 def test_inline_asm_wait_states(source):
     asm = _assembly(os.path.join(ROOT, "exact_attention_flash_amd", "csrc", source))
     kernels = re.findall(r"^(_Z\S+):\s*(?:;|$)", asm, re.M)

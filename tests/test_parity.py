@@ -91,13 +91,36 @@ def _sample_rows(n, count, rng):
     return np.array(sorted(rows))
 
 
+def _item_rows(n, h, rng):
+    """One row of every 256-row query tile of slice h (the kernels' work item is a
+    (slice, 256-row query tile) pair), at an in-tile offset that walks the eight
+    32-row blocks the eight waves of a workgroup own as the slice and tile change,
+    plus the tile and wave boundaries and a few random rows."""
+    tiles = (n + 255) // 256
+    rows = set()
+    for t in range(tiles):
+        blk = (h + t) % 8
+        r = 256 * t + 32 * blk + (7 * h + 13 * t) % 32
+        rows.add(min(r, n - 1))
+    rows.update(_sample_rows(n, 8, rng).tolist())
+    return np.array(sorted(rows))
+
+
 CASES = [(name, c) for name, w in inputs.WORKLOADS.items() for c in w.causal]
+# the headline shape without the mask: long items that cross into the next item of
+# the same workgroup with every wave active (not one of the measured workloads)
+EXTRA = {"llama7b_b2_h32_n4096_d128_noncausal": inputs.Workload(
+    "llama7b_b2_h32_n4096_d128_noncausal", 2, 32, 4096, 128, inputs.BF16, 1.0, (False,), 3)}
+CASES += [(name, c) for name, w in EXTRA.items() for c in w.causal]
 
 
 @pytest.mark.parametrize("seed_offset", [0, 100])
 @pytest.mark.parametrize("name,causal", CASES)
 def test_workload_parity(fa, name, causal, seed_offset):
-    w = inputs.WORKLOADS[name]
+    """Full size, in the launch configuration the benchmark times: complete outputs
+    where the oracle is quick, otherwise at least one row of every work item
+    (slice, 256-row query tile) of every slice, plus complete slices."""
+    w = inputs.WORKLOADS[name] if name in inputs.WORKLOADS else EXTRA[name]
     t0 = time.time()
     qb, kb, vb = inputs.workload_qkv(w, seed_offset)
     scale = inputs.default_scale(w.d)
@@ -114,24 +137,46 @@ def test_workload_parity(fa, name, causal, seed_offset):
         assert_parity(m, name)
         return
     rng = np.random.default_rng(w.seed + seed_offset)
-    rows = _sample_rows(w.N, 24, rng)
     go, gl, ro_all, rl_all = [], [], [], []
+    n_rows = 0
     for h in range(bh):
+        rows = _item_rows(w.N, h, rng)
+        n_rows += len(rows)
         ro, rl = _oracle(qb, kb, vb, w.dtype, causal, scale, rows=rows, heads=[h])
         go.append(o[h, rows])
         gl.append(lse[h, rows])
         ro_all.append(ro[0])
         rl_all.append(rl[0])
-    m = metrics(np.stack(go), np.stack(gl), np.stack(ro_all), np.stack(rl_all), w.dtype)
-    _log(f"  sampled {len(rows)} rows x {bh} slices {time.time() - t0:.1f}s: {m}")
+    m = metrics(np.concatenate(go), np.concatenate(gl), np.concatenate(ro_all), np.concatenate(rl_all), w.dtype)
+    _log(f"  {n_rows} rows covering every (slice, 256-row query tile) of {bh} slices {time.time() - t0:.1f}s: {m}")
     assert_parity(m, f"{name} sampled rows")
-    # complete heads: first and last (batch, head) slice when the oracle is quick enough
-    full_heads = [0, bh - 1] if w.N <= 4099 else []
+    # complete slices: the first and last (batch, head) slice, and one slice of the
+    # long-context workload
+    full_heads = [0, bh - 1] if w.N <= 4099 else [bh // 2]
     for h in full_heads:
         ro, rl = _oracle(qb, kb, vb, w.dtype, causal, scale, heads=[h])
         m = metrics(o[h], lse[h], ro[0], rl[0], w.dtype)
         _log(f"  full slice {h} {time.time() - t0:.1f}s: {m}")
         assert_parity(m, f"{name} slice {h}")
+
+
+# Several work items per workgroup (the persistent grid has one workgroup per
+# compute unit): the tile stream and the pipeline run across item boundaries.
+MULTI_ITEM_SHAPES = [(8, 32, 512, 128), (16, 32, 512, 64), (6, 32, 704, 128)]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", [inputs.BF16, inputs.FP16])
+@pytest.mark.parametrize("shape", MULTI_ITEM_SHAPES)
+def test_multi_item_workgroups_full(fa, shape, dtype, causal):
+    seed = 2000 + 11 * MULTI_ITEM_SHAPES.index(shape) + (3 if causal else 0) + (1 if dtype == inputs.FP16 else 0)
+    qb, kb, vb = inputs.draw_qkv(shape, dtype, 1.0, seed)
+    scale = inputs.default_scale(shape[-1])
+    o, lse = _run_gpu(fa, qb, kb, vb, dtype, causal, scale)
+    ro, rl = _oracle(qb, kb, vb, dtype, causal, scale)
+    m = metrics(o, lse, ro, rl, dtype)
+    _log(f"multi-item {shape} {dtype} causal={causal}: {m}")
+    assert_parity(m, f"{shape} {dtype} causal={causal}")
 
 
 @pytest.mark.parametrize("dtype", [inputs.BF16, inputs.FP16])
