@@ -227,39 +227,46 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_sp(FwdArgs a) {
   }
 
   // Tile-stream cursors of the K and V loads: item rank r, item j (-1 once the
-  // stream is exhausted), tile t of the item's n, the slice's base and extent.
+  // stream is exhausted), tile t of the item's n, the address of tile t and the bytes
+  // from there to the end of the slice (the load descriptor's range), and the bytes
+  // per tile. Rebuilt (and made wave-uniform) when the cursor enters an item,
+  // advanced by one tile step otherwise.
   struct Cursor {
     int r, j, t, n;
     const char* base;
-    uint32_t ext, step;
+    uint32_t rem, step;
   };
   auto cursor_item = [&](Cursor& c, bool is_k) {
     if (c.j < 0) return;
     KArgs* ka = kargs();
+    const char* b;
     if (is_k) {
-      c.base = reinterpret_cast<const char*>(reinterpret_cast<const uint16_t*>(ka->k) +
-                                             slice_off(item_bh(c.j), ka->k_sb, ka->k_sh));
-      c.ext = ka->k_ext;
+      b = reinterpret_cast<const char*>(reinterpret_cast<const uint16_t*>(ka->k) +
+                                        slice_off(item_bh(c.j), ka->k_sb, ka->k_sh));
+      c.rem = ka->k_ext;
       c.step = (uint32_t)(kBN * 2 * ka->k_sn);
     } else {
-      c.base = reinterpret_cast<const char*>(reinterpret_cast<const uint16_t*>(ka->v) +
-                                             slice_off(item_bh(c.j), ka->v_sb, ka->v_sh));
-      c.ext = ka->v_ext;
+      b = reinterpret_cast<const char*>(reinterpret_cast<const uint16_t*>(ka->v) +
+                                        slice_off(item_bh(c.j), ka->v_sb, ka->v_sh));
+      c.rem = ka->v_ext;
       c.step = (uint32_t)(kBN * 2 * ka->v_sn);
     }
+    c.base = uniform_ptr(b);
+    c.rem = __builtin_amdgcn_readfirstlane(c.rem);
+    c.step = __builtin_amdgcn_readfirstlane(c.step);
     c.t = 0;
-    c.n = item_tiles(item_q0(c.j));
+    c.n = __builtin_amdgcn_readfirstlane(item_tiles(item_q0(c.j)));
   };
   auto cursor_advance = [&](Cursor& c, bool is_k) {
     if (++c.t == c.n) {
       c.j = item_index(++c.r);
       cursor_item(c, is_k);
+    } else {
+      c.base += c.step;
+      c.rem -= c.step;
     }
   };
-  auto cursor_rsrc = [&](const Cursor& c) {
-    const uint32_t off = (uint32_t)c.t * c.step;
-    return uniform_rsrc(c.base + off, c.ext - off);
-  };
+  auto cursor_rsrc = [&](const Cursor& c) { return buffer_rsrc(c.base, c.rem); };
   Cursor kc{0, first_j, 0, 0, nullptr, 0, 0}, vc{0, first_j, 0, 0, nullptr, 0, 0};
   cursor_item(kc, true);
   cursor_item(vc, false);
@@ -460,8 +467,19 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_sp(FwdArgs a) {
       });
     };
     constexpr int kTicksPerStep = 32 / kSteps;  // 1 at D = 128, 2 at D = 64
+    // The two waves of a SIMD run the same stream at the same time; the issue
+    // arbiter favours the older one (waves 0-3), which would finish its products
+    // early and wait at the barrier while the other runs alone. Waves 4-7 get the
+    // higher issue priority for the first half of the products, waves 0-3 for the
+    // second. (The choice is made inside the asm statement so that the compiler sees
+    // no branch on the wave index.)
+    asm volatile("s_cmp_lt_u32 %0, 4\n\ts_cbranch_scc1 .Lprio_a%=\n\ts_setprio 1\n.Lprio_a%=:" ::"s"(wave) : "scc");
     static_for<kSteps>([&](auto stc) {
       constexpr int st = decltype(stc)::value;
+      if constexpr (st == kSteps / 2) {
+        asm volatile("s_setprio 1\n\ts_cmp_lt_u32 %0, 4\n\ts_cbranch_scc1 .Lprio_b%=\n\ts_setprio 0\n.Lprio_b%=:" ::"s"(wave)
+                     : "scc");
+      }
       constexpr bool is_s = step_is_s_n<G::nS>(st);
       constexpr int j = step_index_n<G::nS>(st);
       if constexpr (is_s) {
@@ -483,6 +501,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_sp(FwdArgs a) {
     });
     tick(std::integral_constant<int, 32>{});
     tick(std::integral_constant<int, 33>{});
+    __builtin_amdgcn_s_setprio(0);
     return sum;
   };
 
@@ -747,24 +766,20 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_sp(FwdArgs a) {
   // the loads (K three tiles ahead, V one) stay inside the item. The plan of each next
   // iteration (reference choice from the lane maximum of the new scores) is taken
   // before the barrier; the iteration after the run is planned in full.
-  auto steady_iter = [&](auto pc, const char*& kb, uint32_t& kn, const char*& vb, uint32_t& vn) {
+  auto steady_iter = [&](auto pc) {
     constexpr int P = decltype(pc)::value;
     const int c3w = c3 == 0 ? 2 : c3 - 1;
     const int c3v = c3 == 2 ? 0 : c3 + 1;
-    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(kb, kn);
-    const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(vb, vn);
-    const float sum = block(pc, pl_ref, c3 * G::tileBytes, G::vRing + c3v * G::tileBytes, kr, vr,
-                            kring + c3w * G::tileBytes, vring + c3 * G::tileBytes);
+    const float sum = block(pc, pl_ref, c3 * G::tileBytes, G::vRing + c3v * G::tileBytes, cursor_rsrc(kc),
+                            cursor_rsrc(vc), kring + c3w * G::tileBytes, vring + c3 * G::tileBytes);
     l_run = pl_alpha * l_run + sum;
     m_run = pl_m;
     if (pl_exact) {
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) acc[db] *= pl_alpha;
     }
-    kb += kc.step;
-    kn -= kc.step;
-    vb += vc.step;
-    vn -= vc.step;
+    cursor_advance(kc, true);
+    cursor_advance(vc, false);
     c3 = c3v;
     ++g;
     // plan of the next iteration (steady: all slots, no mask): sb[P] holds its scores
@@ -785,24 +800,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_sp(FwdArgs a) {
     const int t0 = g - c_start;
     const int t_end = min(c_fl, c_n - 4);
     if (!(c_j >= 0 && t0 >= 2 && t0 + 1 <= t_end)) return;
-    // the planned iteration is steady (it has no mask, no exact first tile): pl_* hold
-    // its reference choice
-    const char* kb = kc.base + (uint32_t)kc.t * kc.step;
-    uint32_t kn = kc.ext - (uint32_t)kc.t * kc.step;
-    const char* vb = vc.base + (uint32_t)vc.t * vc.step;
-    uint32_t vn = vc.ext - (uint32_t)vc.t * vc.step;
+    // the planned iteration is steady (no mask, not an item's first tile): pl_* hold
+    // its reference choice; the loads stay inside the item until the run ends
     int t = t0;
     do {
-      steady_iter(ic<0>{}, kb, kn, vb, vn);
-      steady_iter(ic<1>{}, kb, kn, vb, vn);
+      steady_iter(ic<0>{});
+      steady_iter(ic<1>{});
       t += 2;
     } while (t + 1 <= t_end);
-    // the cursors' last tiles in the run were the item's (K may now stand at its end:
-    // advance the last step through the cursor so that it moves to the next item)
-    kc.t += t - t0 - 1;
-    vc.t += t - t0 - 1;
-    cursor_advance(kc, true);
-    cursor_advance(vc, false);
     plan(ic<0>{});
   };
 

@@ -70,11 +70,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 // registers as the descriptor operand of a load requires (free when they already
 // are; needed where the compiler cannot prove a value built under a branch on the
 // wave index uniform).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t b = (uint64_t)(uintptr_t)base;
+// A wave-uniform copy of an address in scalar registers. readfirstlane yields an
+// int: each half goes through uint32_t before the halves are joined, because a
+// signed low half would be sign-extended over the high half whenever its bit 31 is
+// set (an unmapped address for every buffer placed there).
+template <class T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t b = (uint64_t)(uintptr_t)p;
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
-  return buffer_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo), __builtin_amdgcn_readfirstlane(bytes));
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, uint32_t bytes) {
+  return buffer_rsrc(uniform_ptr(base), __builtin_amdgcn_readfirstlane(bytes));
 }
 
 __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {

@@ -95,20 +95,50 @@ def _regs(text: str):
     return out
 
 
+_LABEL = re.compile(r"^(\.L[\w$.]+):")
+_BRANCH = re.compile(r"^s_(c?branch\w*)\s+(\.L[\w$.]+)")
+
+
 def _function(asm: str, kernel: str):
-    m = re.search(r"^" + re.escape(kernel) + r":(.*?)s_endpgm", asm, re.S | re.M)
+    """The kernel's code as basic blocks with their control-flow edges. Every label
+    starts a block (the compiler's and those of asm statements that branch inside
+    themselves); a block ends at a label or after a branch. Returns (blocks, succ,
+    pred): instruction lists and successor / predecessor block indices."""
+    m = re.search(r"^" + re.escape(kernel) + r":(.*?)^\.Lfunc_end", asm, re.S | re.M)
     assert m, kernel
-    blocks, cur = [], []
+    blocks, labels, cur, cur_label = [], {}, [], None
+
+    def close():
+        labels.setdefault(cur_label, len(blocks)) if cur_label else None
+        blocks.append(cur)
+
     for ln in m.group(1).split("\n"):
-        if re.match(r"^\.LBB\S+:", ln):
-            blocks.append(cur)
-            cur = []
+        lm = _LABEL.match(ln.strip())
+        if lm:
+            close()
+            cur, cur_label = [], lm.group(1)
             continue
         t = ln.split(";")[0].strip()
         if t and not t.startswith("."):
             cur.append(t)
-    blocks.append(cur)
-    return blocks
+            if t.startswith(("s_branch", "s_cbranch", "s_endpgm", "s_setpc")):
+                close()
+                cur, cur_label = [], None
+    close()
+    succ = [[] for _ in blocks]
+    for i, blk in enumerate(blocks):
+        last = blk[-1] if blk else ""
+        bm = _BRANCH.match(last)
+        if bm:
+            assert bm.group(2) in labels, f"{kernel}: branch to unknown label {bm.group(2)}"
+            succ[i].append(labels[bm.group(2)])
+        if not last.startswith(("s_branch ", "s_setpc", "s_endpgm")) and i + 1 < len(blocks):
+            succ[i].append(i + 1)
+    pred = [[] for _ in blocks]
+    for i, ss in enumerate(succ):
+        for j in ss:
+            pred[j].append(i)
+    return blocks, succ, pred
 
 
 def _waits(ins: str) -> int:
@@ -126,47 +156,92 @@ def _is_valu(op: str) -> bool:
     return op.startswith("v_") and "mfma" not in op
 
 
+def _window(cfg, b, n, need, backward):
+    """Every instruction within `need` wait states before (after) instruction n of
+    block b, on every path through the control-flow graph, with the wait states
+    between: a list of (instruction, wait states). A window that reaches the start of
+    the kernel ends there (nothing ran before it)."""
+    blocks, succ, pred = cfg
+    out, seen = [], set()
+    stack = [(b, n, 0)]
+    while stack:
+        b, n, w = stack.pop()
+        blk = blocks[b]
+        seq = reversed(blk[:n]) if backward else blk[n + 1:]
+        for ins in seq:
+            if w >= need:
+                break
+            out.append((ins, w))
+            w += _waits(ins)
+        else:
+            for nb in (pred[b] if backward else succ[b]):
+                key = (nb, w)
+                if key not in seen:
+                    seen.add(key)
+                    stack.append((nb, len(blocks[nb]) if backward else -1, w))
+    return out
+
+
 def _hazards(asm: str, kernel: str):
-    """Violations in one kernel: LDS-DMA loads without five wait states after a VALU
-    write of an SGPR they read; MFMAs without two after a VALU write of a source;
-    VALU accesses of an MFMA result within twelve wait states of the MFMA."""
+    """Violations in one kernel, on every control-flow path: LDS-DMA loads without
+    five wait states after a VALU write of an SGPR they read; MFMAs without two after
+    a VALU write of a source; VALU accesses of an MFMA result within twelve wait
+    states of the MFMA."""
     bad = []
-    for blk in _function(asm, kernel):
+    cfg = _function(asm, kernel)
+    for b, blk in enumerate(cfg[0]):
         for n, ins in enumerate(blk):
             op = ins.split()[0]
             ops = _operands(ins)
             if op.startswith("buffer_load") and ins.endswith("lds"):
                 reads = _regs(",".join(ops[1:]))
-                w = 0
-                for prev in reversed(blk[:n]):
-                    if w >= 5:
-                        break
-                    pop = prev.split()[0]
-                    if _is_valu(pop) and _regs(_operands(prev)[0]) & reads:
+                for prev, w in _window(cfg, b, n, 5, True):
+                    if _is_valu(prev.split()[0]) and _regs(_operands(prev)[0]) & reads:
                         bad.append(f"{kernel}: '{prev}' then '{ins}' within {w} wait states")
-                    w += _waits(prev)
-                if w < 5:  # the window reaches a block start: the predecessor is unknown
-                    bad.append(f"{kernel}: '{ins}' only {w} wait states into its block")
             elif "mfma" in op:
                 srcs = _regs(",".join(ops[1:3]))
-                w = 0
-                for prev in reversed(blk[:n]):
-                    if w >= 2:
-                        break
+                for prev, w in _window(cfg, b, n, 2, True):
                     pop = prev.split()[0]
                     if (_is_valu(pop) or pop.startswith("v_accvgpr_write")) and _regs(_operands(prev)[0]) & srcs:
                         bad.append(f"{kernel}: '{prev}' then '{ins}' within {w} wait states")
-                    w += _waits(prev)
                 dst = _regs(ops[0])
-                w = 0
-                for nxt in blk[n + 1:]:
-                    if w >= 12:
-                        break
-                    nop = nxt.split()[0]
-                    if _is_valu(nop) and _regs(",".join(_operands(nxt))) & dst:
+                for nxt, w in _window(cfg, b, n, 12, False):
+                    if _is_valu(nxt.split()[0]) and _regs(",".join(_operands(nxt))) & dst:
                         bad.append(f"{kernel}: '{ins}' then '{nxt}' within {w} wait states")
-                    w += _waits(nxt)
     return bad
+
+
+def test_hazard_windows_follow_control_flow():
+    """The audit follows a window across branches: a VALU read of an MFMA result in
+    the block a branch leads to, or a VALU write of a load's descriptor at the end of
+    a predecessor, is found (synthetic listings, no compiler needed)."""
+    fwd = "\n".join(["_k:", "v_mfma_f32_32x32x16_bf16 v[0:15], v[16:19], v[20:23], v[0:15]",
+                       "s_cbranch_scc1 .LBB0_2", "s_nop 15", ".LBB0_2:", "v_add_f32 v30, v3, v4", "s_endpgm", ".Lfunc_end0:"])
+    assert any("v_add_f32 v30, v3, v4" in x for x in _hazards(fwd, "_k"))
+    fine = fwd.replace("s_cbranch_scc1 .LBB0_2", "s_nop 11\ns_cbranch_scc1 .LBB0_2")
+    assert not _hazards(fine, "_k")
+    back = "\n".join(["_k:", "v_readfirstlane_b32 s4, v1", "s_branch .LBB0_1", ".LBB0_1:",
+                       "buffer_load_dwordx4 v2, s[4:7], 0 offen lds", "s_endpgm", ".Lfunc_end0:"])
+    assert any("v_readfirstlane_b32 s4" in x for x in _hazards(back, "_k"))
+    loop = "\n".join(["_k:", "s_nop 7", ".LBB0_1:", "buffer_load_dwordx4 v2, s[4:7], 0 offen lds",
+                       "v_readfirstlane_b32 s4, v1", "s_cbranch_scc1 .LBB0_1", "s_endpgm", ".Lfunc_end0:"])
+    assert any("v_readfirstlane_b32 s4" in x for x in _hazards(loop, "_k"))
+
+
+def test_uniform_addresses_are_not_sign_extended():
+    """readfirstlane yields an int: widening it straight into a 64-bit address
+    sign-extends a low half with bit 31 set over the high half (an unmapped
+    address). Every address made wave-uniform goes through 32-bit unsigned halves."""
+    csrc = os.path.join(ROOT, "exact_attention_flash_amd", "csrc")
+    pat = re.compile(r"(\(\s*u?int64_t\s*\)|static_cast<\s*u?int64_t\s*>\(|\|)\s*__builtin_amdgcn_readfirstlane")
+    bad = []
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            text = re.sub(r"\s+", " ", open(os.path.join(csrc, f)).read())
+            bad += [f"{f}: ...{text[max(0, m.start() - 60):m.end() + 20]}..." for m in pat.finditer(text)]
+    assert not bad, "\n".join(bad)
+    bad_src = "x = ((uint64_t)__builtin_amdgcn_readfirstlane(hi) << 32) | __builtin_amdgcn_readfirstlane(lo);"
+    assert pat.search(bad_src)
 
 
 @pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
@@ -180,6 +255,6 @@ def test_inline_asm_wait_states(source):
     bad = []
     for k in kernels:
         bad += _hazards(asm, k)
-        lds_loads += sum(1 for blk in _function(asm, k) for i in blk if i.startswith("buffer_load") and i.endswith("lds"))
+        lds_loads += sum(1 for blk in _function(asm, k)[0] for i in blk if i.startswith("buffer_load") and i.endswith("lds"))
     assert lds_loads > 0
     assert not bad, "\n".join(bad[:20]) + f"\n({len(bad)} in all)"
