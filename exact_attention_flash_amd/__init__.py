@@ -12,10 +12,11 @@ import math
 from . import _native
 from ._native import (FA_BF16, FA_FP16, FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEADDIM,  # noqa: F401
                       FA_ERR_DTYPE, FA_ERR_SCALE, FA_ERR_ALIGN, FA_ERR_ALIAS, FA_ERR_HIP, FA_ERR_ARG,
-                      FA_ERR_WORKSPACE, FA_ERR_STRIDE, FA_FP8_ROWS, FA_FP8_KEYS_T)
+                      FA_ERR_WORKSPACE, FA_ERR_STRIDE, FA_ERR_SCRATCH, FA_SPLITKV_SCRATCH_BYTES,
+                      FA_FP8_ROWS, FA_FP8_KEYS_T)
 
 __all__ = ["forward", "backward", "forward_splitkv", "flash_attn_fwd", "flash_attn_fwd_strided",
-           "flash_attn_fwd_splitkv", "flash_attn_bwd",
+           "flash_attn_fwd_splitkv", "flash_attn_fwd_splitkv_noalloc", "flash_attn_bwd",
            "splitkv_plan", "splitkv_workspace_size", "quantize_fp8", "flash_attn_fwd_fp8", "forward_fp8",
            "flash_attn_strerror", "flash_attn_abi_version"]
 
@@ -184,6 +185,27 @@ def flash_attn_fwd_splitkv(q, k, v, o, lse, workspace, causal: bool = False, sca
                              B, H, N, d, causal, scale, num_splits, ws, ws_bytes, stream.cuda_stream, dtype)
     if st != FA_OK:
         raise FlashAttnError(st, "flash_attn_fwd_splitkv")
+
+
+def flash_attn_fwd_splitkv_noalloc(q, k, v, o, lse, causal: bool = False, scale: float | None = None,
+                                   num_splits: int = 0, stream=None) -> None:
+    """The key-split forward with its partial results in the library's fixed device
+    array (FA_SPLITKV_SCRATCH_BYTES per GPU) instead of a workspace: no device memory
+    is allocated by the call. Calls that overlap in time on one GPU race."""
+    import torch
+
+    _check_fwd_tensors(q, k, v, o, lse)
+    B, H, N, d = q.shape
+    dtype = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        st = _native.splitkv_noalloc_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                         B, H, N, d, causal, scale, num_splits, stream.cuda_stream, dtype)
+    if st != FA_OK:
+        raise FlashAttnError(st, "flash_attn_fwd_splitkv_noalloc")
 
 
 def forward_splitkv(q, k, v, causal: bool = False, scale: float | None = None, num_splits: int = 0,

@@ -21,6 +21,10 @@ FA_ERR_HIP = -8
 FA_ERR_ARG = -9
 FA_ERR_WORKSPACE = -10
 FA_ERR_STRIDE = -11
+FA_ERR_SCRATCH = -12
+
+# bytes of the library's fixed partial-result array (FA_SPLITKV_SCRATCH_BYTES)
+FA_SPLITKV_SCRATCH_BYTES = 65 * 1024 * 1024
 
 FA_FP8_ROWS = 0
 FA_FP8_KEYS_T = 1
@@ -77,6 +81,12 @@ def lib() -> ctypes.CDLL:
         L.flash_attn_fwd_splitkv_plan.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int, ctypes.c_int]
         L.flash_attn_fwd_splitkv_workspace_size.restype = ctypes.c_int64
         L.flash_attn_fwd_splitkv_workspace_size.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int, ctypes.c_int]
+        L.flash_attn_fwd_splitkv_noalloc.restype = ctypes.c_int
+        L.flash_attn_fwd_splitkv_noalloc.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+        ]
         L.flash_attn_bwd.restype = ctypes.c_int
         L.flash_attn_bwd.argtypes = [ctypes.c_void_p] * 10 + [
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
@@ -153,6 +163,12 @@ def validate_splitkv_raw(q, k, v, o, lse, B, H, N, d, causal, scale, num_splits,
     """Call flash_attn_fwd_splitkv_validate (host checks only, never launches)."""
     return lib().flash_attn_fwd_splitkv_validate(q, k, v, o, lse, B, H, N, d, int(causal), float(scale),
                                                  int(num_splits), ws, int(ws_bytes), stream, dtype)
+
+
+def splitkv_noalloc_raw(q, k, v, o, lse, B, H, N, d, causal, scale, num_splits, stream, dtype) -> int:
+    """Call flash_attn_fwd_splitkv_noalloc with integer addresses; returns the status code."""
+    return lib().flash_attn_fwd_splitkv_noalloc(q, k, v, o, lse, B, H, N, d, int(causal), float(scale),
+                                                int(num_splits), stream, dtype)
 
 
 def splitkv_plan(B, H, N, d, causal, cus) -> int:

@@ -20,6 +20,7 @@ SOURCES = [
     os.path.join(PKG_DIR, "csrc", "bwd_kernel.hip"),
     os.path.join(PKG_DIR, "csrc", "fp8_quant.hip"),
     os.path.join(PKG_DIR, "csrc", "fwd_fp8.hip"),
+    os.path.join(PKG_DIR, "csrc", "noalloc.hip"),
     os.path.join(PKG_DIR, "csrc", "flash_attn.cpp"),
 ]
 # Packed fp32 VALU instructions are disabled for device code: the compiler

@@ -38,7 +38,7 @@ hipError_t launch_unsplit(const fa::FwdArgs& a, bool fp16, int d, bool causal, h
 
 }  // namespace
 
-extern "C" int flash_attn_abi_version(void) { return 5; }
+extern "C" int flash_attn_abi_version(void) { return 6; }
 
 extern "C" const char* flash_attn_strerror(int status) {
   switch (status) {
@@ -56,6 +56,7 @@ extern "C" const char* flash_attn_strerror(int status) {
     case FA_ERR_STRIDE:
       return "a stride is negative, not a multiple of 8 elements, a row stride is below d or too large, a slice "
              "spans 2 GiB or more, or an output overlaps itself";
+    case FA_ERR_SCRATCH: return "the split needs more partial-result memory than the library's fixed array holds";
     default: return "unknown status";
   }
 }

@@ -48,10 +48,19 @@ typedef enum {
   FA_ERR_HIP = -8,     /* the HIP runtime reported an error at launch             */
   FA_ERR_ARG = -9,     /* causal is not 0 or 1, or num_splits is negative        */
   FA_ERR_WORKSPACE = -10, /* split workspace NULL, not 16-byte aligned or too small */
-  FA_ERR_STRIDE = -11  /* strided call: a stride negative, not a multiple of 8 elements, a row
+  FA_ERR_STRIDE = -11, /* strided call: a stride negative, not a multiple of 8 elements, a row
                           stride below d or >= 2^23, a slice spanning >= 2 GiB, or o / lse
                           overlapping itself                                         */
+  FA_ERR_SCRATCH = -12 /* flash_attn_fwd_splitkv_noalloc: the split needs more than
+                          FA_SPLITKV_SCRATCH_BYTES of partial results             */
 } fa_status;
+
+/* Bytes of the library's own device array that flash_attn_fwd_splitkv_noalloc
+ * keeps its partial results in (65 MiB per GPU). Every split that
+ * flash_attn_fwd_splitkv_plan picks for d <= 128 on a device of up to 256
+ * compute units fits: it makes fewer than 2 * cus work items of at most 256
+ * rows, so at most 2 * 256 * 256 * 129 * 4 bytes (64.5 MiB) of partials. */
+#define FA_SPLITKV_SCRATCH_BYTES (65u * 1024u * 1024u)
 
 /*
  * flash_attn_fwd -- exact attention forward on one stream.
@@ -277,6 +286,32 @@ int64_t flash_attn_fwd_splitkv_workspace_size(int64_t B, int64_t H, int64_t N, i
                                               int num_splits);
 
 /*
+ * flash_attn_fwd_splitkv_noalloc -- flash_attn_fwd_splitkv for callers that cannot
+ * allocate device memory at the call (code under stream capture, serving loops or
+ * harnesses that forbid allocation): the same computation, kernels and result,
+ * with the partial outputs and log-sum-exps kept in a device array of the library
+ * (FA_SPLITKV_SCRATCH_BYTES, one copy per GPU, held from the first use of the
+ * library on that GPU until the process ends) instead of a caller workspace.
+ *
+ * Arguments q, k, v, o, lse, B, H, N, d, causal, scale, num_splits, stream, dtype:
+ * as for flash_attn_fwd_splitkv. The call allocates and frees nothing; on the
+ * first call on a device it looks up that device's copy of the array (the current
+ * device at the call).
+ * Errors: as for flash_attn_fwd_splitkv, plus FA_ERR_SCRATCH when the resolved
+ * split needs more than FA_SPLITKV_SCRATCH_BYTES (nothing is launched), and
+ * FA_ERR_HIP when the array's address cannot be obtained. A resolved count of 1
+ * runs flash_attn_fwd and leaves the array untouched.
+ * Concurrency: every call on one GPU shares that GPU's array, and a call leaves
+ * its partials there; calls that overlap in time on one GPU (different streams,
+ * or host threads without ordering between their streams) race and may return
+ * wrong results. Calls ordered on one stream are safe: nothing in the array needs
+ * clearing between them, since each call writes every partial it reads.
+ */
+int flash_attn_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                   int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
+                                   int num_splits, void* stream, int dtype);
+
+/*
  * flash_attn_bwd -- gradients of the forward pass with respect to q, k and v.
  *
  * For the loss gradient dout = dL/do of o = flash_attn_fwd(q, k, v), with
@@ -327,8 +362,9 @@ int flash_attn_bwd_validate(const void* q, const void* k, const void* v, const v
 /* Static, never-freed description of a status code (unknown codes included). */
 const char* flash_attn_strerror(int status);
 
-/* ABI version of this header, currently 5 (1: forward only; 2: + backward;
- * 3: + key-split forward; 4: + strided forward; 5: + FP8 quantization and forward). */
+/* ABI version of this header, currently 6 (1: forward only; 2: + backward;
+ * 3: + key-split forward; 4: + strided forward; 5: + FP8 quantization and forward;
+ * 6: + key-split forward without a caller workspace). */
 int flash_attn_abi_version(void);
 
 #ifdef __cplusplus

@@ -36,7 +36,8 @@ def test_library_loads_and_exports_header_symbols():
     names = _declared_functions()
     assert names == ["flash_attn_abi_version", "flash_attn_bwd", "flash_attn_bwd_validate", "flash_attn_fwd",
                      "flash_attn_fwd_fp8", "flash_attn_fwd_fp8_validate",
-                     "flash_attn_fwd_splitkv", "flash_attn_fwd_splitkv_plan", "flash_attn_fwd_splitkv_validate",
+                     "flash_attn_fwd_splitkv", "flash_attn_fwd_splitkv_noalloc", "flash_attn_fwd_splitkv_plan",
+                     "flash_attn_fwd_splitkv_validate",
                      "flash_attn_fwd_splitkv_workspace_size", "flash_attn_fwd_strided",
                      "flash_attn_fwd_strided_validate", "flash_attn_fwd_validate", "flash_attn_quantize_fp8",
                      "flash_attn_quantize_fp8_validate", "flash_attn_strerror"]
@@ -49,10 +50,10 @@ def test_library_loads_and_exports_header_symbols():
 
 
 def test_abi_version_and_strerror():
-    assert fa.flash_attn_abi_version() == 5
+    assert fa.flash_attn_abi_version() == 6
     codes = [fa.FA_OK, fa.FA_ERR_NULL, fa.FA_ERR_SHAPE, fa.FA_ERR_HEADDIM, fa.FA_ERR_DTYPE,
              fa.FA_ERR_SCALE, fa.FA_ERR_ALIGN, fa.FA_ERR_ALIAS, fa.FA_ERR_HIP, fa.FA_ERR_ARG,
-             fa.FA_ERR_WORKSPACE, fa.FA_ERR_STRIDE]
+             fa.FA_ERR_WORKSPACE, fa.FA_ERR_STRIDE, fa.FA_ERR_SCRATCH]
     msgs = [fa.flash_attn_strerror(c) for c in codes]
     assert len(set(msgs)) == len(codes)
     assert fa.flash_attn_strerror(12345) == "unknown status"
@@ -283,6 +284,56 @@ def test_splitkv_validate_accepts(kw):
 def test_splitkv_empty_problem_is_a_noop(kw):
     assert _native.splitkv_raw(*_sargs(q=None, k=None, v=None, o=None, lse=None, ws=None, ws_bytes=0,
                                        **kw)) == fa.FA_OK
+
+
+# ---- key-split forward without a workspace ----
+# Only calls that fail a check (or describe an empty problem) are made: they return
+# before any HIP call. num_splits = 0 would query the device, so it is not used here.
+
+def _nargs(q=A, k=A + GB, v=A + 2 * GB, o=A + 3 * GB, lse=A + 4 * GB, B=1, H=1, N=1024, d=64, causal=0,
+           scale=0.125, num_splits=4, stream=None, dtype=0):
+    return (q, k, v, o, lse, B, H, N, d, causal, scale, num_splits, stream, dtype)
+
+
+def test_noalloc_boundary_sizes():
+    assert fa.splitkv_workspace_size(1, 16, 1024, 64, 0, 16) == fa.FA_SPLITKV_SCRATCH_BYTES
+    assert fa.splitkv_workspace_size(1, 16, 1025, 64, 0, 16) > fa.FA_SPLITKV_SCRATCH_BYTES
+
+
+def test_noalloc_scratch_size_matches_header_and_covers_the_planned_split():
+    text = open(HEADER).read()
+    m = re.search(r"#define FA_SPLITKV_SCRATCH_BYTES \((\d+)u \* 1024u \* 1024u\)", text)
+    assert m and int(m.group(1)) * 1024 * 1024 == fa.FA_SPLITKV_SCRATCH_BYTES
+    # every split the planner picks for a 256-compute-unit device fits, at both head sizes
+    worst = 0
+    for d in (64, 128):
+        for causal in (0, 1):
+            for B, H in ((1, 1), (1, 2), (1, 3), (1, 5), (2, 3), (1, 8), (3, 7), (1, 64), (4, 32)):
+                for N in (449, 512, 1000, 1024, 2047, 4096, 8191, 16384, 65536):
+                    s = fa.splitkv_plan(B, H, N, d, causal, 256)
+                    worst = max(worst, fa.splitkv_workspace_size(B, H, N, d, causal, s))
+    assert 0 < worst <= fa.FA_SPLITKV_SCRATCH_BYTES
+
+
+BAD_NOALLOC = [
+    (dict(num_splits=-1), fa.FA_ERR_ARG), (dict(d=96), fa.FA_ERR_HEADDIM), (dict(scale=0.0), fa.FA_ERR_SCALE),
+    (dict(q=None), fa.FA_ERR_NULL), (dict(o=A), fa.FA_ERR_ALIAS), (dict(causal=5), fa.FA_ERR_ARG),
+    (dict(dtype=7), fa.FA_ERR_DTYPE), (dict(B=-1), fa.FA_ERR_SHAPE), (dict(lse=A + 4 * GB + 2), fa.FA_ERR_ALIGN),
+    # 2 splits of B1 H64 N4096 d128 need 2 * 64 * 4096 * 129 * 4 bytes (258 MiB)
+    (dict(H=64, N=4096, d=128, num_splits=2), fa.FA_ERR_SCRATCH),
+    # 16 splits of B1 H16 d64 need exactly 65 MiB at N = 1024; one more row does not fit
+    (dict(H=16, N=1025, d=64, num_splits=16), fa.FA_ERR_SCRATCH),
+]
+
+
+@pytest.mark.parametrize("kw,code", BAD_NOALLOC)
+def test_noalloc_rejects_before_launch(kw, code):
+    assert _native.splitkv_noalloc_raw(*_nargs(**kw)) == code
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0)])
+def test_noalloc_empty_problem_is_a_noop(kw):
+    assert _native.splitkv_noalloc_raw(*_nargs(q=None, k=None, v=None, o=None, lse=None, **kw)) == fa.FA_OK
 
 
 # ---- strided forward ----
