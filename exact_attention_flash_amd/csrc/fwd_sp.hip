@@ -81,6 +81,45 @@ struct Geo {
   __device__ static __forceinline__ int swz(int row) { return chunk_swizzle<D>(row); }
 };
 
+// Division by a run-time invariant divisor d >= 1 of dividends below 2^31 with a
+// multiply-high, an add and a shift: the round-up method of Granlund and Montgomery
+// ("Division by invariant integers using multiplication", 1994). With
+// l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1 (below 2^32),
+// n / d = (mulhi(m, n) + n) >> l; n < 2^31 keeps the sum inside 32 bits.
+struct FastDiv {
+  uint32_t mul, shift;
+};
+constexpr FastDiv make_fastdiv(uint32_t d) {
+  uint32_t l = 0;
+  while ((uint64_t{1} << l) < d) ++l;
+  return FastDiv{(uint32_t)(((uint64_t{1} << 32) * ((uint64_t{1} << l) - d)) / d + 1), l};
+}
+__host__ __device__ constexpr uint32_t fastdiv(uint32_t n, uint32_t mul, uint32_t shift) {
+  return ((uint32_t)(((uint64_t)n * mul) >> 32) + n) >> shift;
+}
+constexpr bool fastdiv_selfcheck() {
+  const uint32_t ns[] = {0u, 1u, 2u, 3u, 7u, 63u, 64u, 65u, 255u, 1000u, 4095u, 65535u, 65536u, 1u << 20,
+                         (1u << 24) + 17u, 123456789u, (1u << 30) + 3u, 2147483646u, 2147483647u};
+  for (uint32_t d = 1; d <= 600; ++d) {
+    const FastDiv f = make_fastdiv(d);
+    for (uint32_t n : ns)
+      if (fastdiv(n, f.mul, f.shift) != n / d) return false;
+    for (uint32_t k = 1; k < 40; ++k) {  // around multiples of d
+      const uint32_t n = d * k * 977u;
+      if (n < 2147483647u && (fastdiv(n, f.mul, f.shift) != n / d || fastdiv(n - 1, f.mul, f.shift) != (n - 1) / d))
+        return false;
+    }
+  }
+  const uint32_t big[] = {1000003u, 65537u, 2147483647u, 1u << 30, 46341u};
+  for (uint32_t d : big) {
+    const FastDiv f = make_fastdiv(d);
+    for (uint32_t n : ns)
+      if (fastdiv(n, f.mul, f.shift) != n / d) return false;
+  }
+  return true;
+}
+static_assert(fastdiv_selfcheck(), "fast division");
+
 using KArgs = const __attribute__((address_space(4))) FwdArgs;
 __device__ __forceinline__ KArgs* kargs() {
   KArgs* p = (KArgs*)(__builtin_amdgcn_kernarg_segment_ptr());
@@ -190,14 +229,16 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_sp(FwdArgs a) {
   const int tiles_all = (N + kBN - 1) / kBN;
   auto slice_off = [&](int bh, int64_t sb, int64_t sh) {
     const int heads = kargs()->heads;
-    return (int64_t)(bh / heads) * sb + (bh % heads) * sh;
+    const int b = (int)fastdiv((uint32_t)bh, a.heads_mul, a.heads_shift);
+    return (int64_t)b * sb + (int64_t)(bh - b * heads) * sh;
   };
   auto item_index = [&](int r) {
     const int j = r * wg_n + ((r & 1) ? wg_n - 1 - wg_k : wg_k);
     return j < n_items ? j : -1;
   };
-  auto item_bh = [&](int j) { return bh_base + j % hpx; };
-  auto item_q0 = [&](int j) { return (CAUSAL ? (a.q_tiles - 1 - j / hpx) : j / hpx) * kBM; };
+  auto grp_div = [&](int j) { return (int)fastdiv((uint32_t)j, a.grp_mul, a.grp_shift); };
+  auto item_bh = [&](int j) { return bh_base + j - grp_div(j) * hpx; };
+  auto item_q0 = [&](int j) { return (CAUSAL ? (a.q_tiles - 1 - grp_div(j)) : grp_div(j)) * kBM; };
   auto item_tiles = [&](int q0) {
     return CAUSAL ? min(tiles_all, (min(q0 + kBM, N) - 1) / kBN + 1) : tiles_all;
   };
@@ -264,6 +305,18 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_sp(FwdArgs a) {
     } else {
       c.base += c.step;
       c.rem -= c.step;
+    }
+  };
+  // one tile step with no item check, and the item check on its own
+  auto cursor_step = [&](Cursor& c) {
+    ++c.t;
+    c.base += c.step;
+    c.rem -= c.step;
+  };
+  auto cursor_settle = [&](Cursor& c, bool is_k) {
+    if (c.t == c.n) {
+      c.j = item_index(++c.r);
+      cursor_item(c, is_k);
     }
   };
   auto cursor_rsrc = [&](const Cursor& c) { return buffer_rsrc(c.base, c.rem); };
@@ -778,8 +831,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_sp(FwdArgs a) {
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) acc[db] *= pl_alpha;
     }
-    cursor_advance(kc, true);
-    cursor_advance(vc, false);
+    // inside a run both cursors stay in the item (the K cursor may step onto its end
+    // in the run's last iteration: fixed up after the run, before the next load)
+    cursor_step(kc);
+    cursor_step(vc);
     c3 = c3v;
     ++g;
     // plan of the next iteration (steady: all slots, no mask): sb[P] holds its scores
@@ -808,6 +863,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_sp(FwdArgs a) {
       steady_iter(ic<1>{});
       t += 2;
     } while (t + 1 <= t_end);
+    cursor_settle(kc, true);
+    cursor_settle(vc, false);
     plan(ic<0>{});
   };
 
@@ -842,6 +899,12 @@ hipError_t launch_fwd_sp(const FwdArgs& args, bool fp16, int d, bool causal, hip
     if (grid < 8) grid = 8;
   }
   a.grid = grid;
+  const FastDiv grp = make_fastdiv((uint32_t)(a.xcd_grouped ? a.bh >> 3 : a.bh));
+  const FastDiv heads = make_fastdiv((uint32_t)a.heads);
+  a.grp_mul = grp.mul;
+  a.grp_shift = grp.shift;
+  a.heads_mul = heads.mul;
+  a.heads_shift = heads.shift;
   if (fp16) {
     if (d == 64) return causal ? launch_one<true, 64, true>(a, stream) : launch_one<true, 64, false>(a, stream);
     return causal ? launch_one<true, 128, true>(a, stream) : launch_one<true, 128, false>(a, stream);
