@@ -157,14 +157,38 @@ using ic = std::integral_constant<int, N>;
 // Order of the products in an iteration: S and P V alternate (S first); S products
 // take all 16-column steps of the first 32-key half before the second half, so the
 // first half of the new scores is complete halfway through.
-template <int NS>
-__device__ constexpr bool step_is_s_n(int st) {
-  return st % 2 == 0;
-}
-template <int NS>
-__device__ constexpr int step_index_n(int st) {
-  return st / 2;
-}
+// Order of one block's products: D/8 S products (two 32-key halves of D/16 steps)
+// and D/8 P V products. The S products sit in a leading region with the P V products
+// spread evenly between them; the block ends with nP/2 - 1 P V products only, so that
+// both halves of the new scores are complete several products before the end and
+// their lane maxima are taken in the VALU slots of those last products.
+template <int D>
+struct Sched {
+  static constexpr int nS = D / 8, nP = D / 8, kSteps = nS + nP;
+  static constexpr int tailP = nP / 2 - 1;
+  static constexpr int region = kSteps - tailP;
+  bool is_s[kSteps];
+  int idx[kSteps];       // index of the step's product among those of its kind
+  int last_s[2];         // step of the last S product of each 32-key half
+  constexpr Sched() : is_s{}, idx{}, last_s{} {
+    const int m = nP - tailP;
+    bool p_at[kSteps] = {};
+    for (int i = 0; i < m; ++i) p_at[(2 * i + 1) * region / (2 * m)] = true;
+    for (int st = region; st < kSteps; ++st) p_at[st] = true;
+    int ns = 0, np = 0;
+    for (int st = 0; st < kSteps; ++st) {
+      is_s[st] = !p_at[st];
+      idx[st] = p_at[st] ? np++ : ns++;
+      if (!p_at[st]) last_s[idx[st] / (nS / 2)] = st;
+    }
+  }
+  constexpr bool valid() const {
+    int ns = 0, np = 0;
+    for (int st = 0; st < kSteps; ++st) (is_s[st] ? ns : np) += 1;
+    return ns == nS && np == nP && last_s[1] + 2 < kSteps && last_s[0] < last_s[1];
+  }
+};
+static_assert(Sched<128>().valid() && Sched<64>().valid(), "block schedule");
 
 // f(integral_constant<int, i>) for i = 0 .. N-1, expanded at compile time (a loop
 // the unroller might leave rolled would index the register arrays dynamically)
@@ -455,24 +479,27 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_sp(FwdArgs a) {
 
   // One iteration's arithmetic as a single instruction stream: S(g+1) into sb[P],
   // the softmax of sb[P^1] against `ref` into pb[P^1] (returns the lane's sum of the
-  // unrounded fp32 probabilities), u += V^T P^T from pb[P], and this wave's share of
-  // the tile loads (K_{g+3} from descriptor kr into kdst, V_{g+1} from vr into vdst).
-  // Products alternate S and P V; each carries one score's softmax work (two at
-  // D = 64), split into three stages two products apart so that no instruction waits
-  // on the one before it; operand reads run kLook products of the same kind ahead.
-  constexpr int kLook = 1;
+  // unrounded fp32 probabilities), u += V^T P^T from pb[P], the lane maximum of the
+  // new scores sb[P] (unmasked, unscaled) into `lmx`, and this wave's share of the
+  // tile loads (K_{g+3} from descriptor kr into kdst, V_{g+1} from vr into vdst).
+  // Products follow Sched<D>; each carries one score's softmax work (two at D = 64),
+  // split into three stages two ticks apart so that no instruction waits on the one
+  // before it; the operand of each product is read two products ahead.
   auto block = [&](auto pc, float ref, int kst, int vst, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
-                   char* kdst, char* vdst) {
+                   char* kdst, char* vdst, float& lmx) {
     constexpr int P = decltype(pc)::value;
     constexpr int Q = P ^ 1;
-    constexpr int kSteps = G::nS + G::nP;
+    constexpr Sched<D> kS{};
+    constexpr int kSteps = Sched<D>::kSteps;
     const int kx = kst + kbase, vx0 = vst + vbase[0], vx1 = vst + vbase[1];
-    u32x4 kop[kLook + 1], vop[kLook + 1];
-#pragma unroll
-    for (int j = 0; j < kLook; ++j) {
-      kop[j] = k_read(kx, j);
-      vop[j] = v_read(vx0, vx1, j);
-    }
+    auto operand = [&](auto stc) -> u32x4 {
+      constexpr int st = decltype(stc)::value;
+      if constexpr (kS.is_s[st]) return k_read(kx, kS.idx[st]);
+      else return v_read(vx0, vx1, kS.idx[st]);
+    };
+    u32x4 op[3];
+    op[0] = operand(std::integral_constant<int, 0>{});
+    op[1] = operand(std::integral_constant<int, 1>{});
     float x[4];
     float sum = 0.f;
     // (each result passes through an empty volatile asm statement: instruction
@@ -503,6 +530,26 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_sp(FwdArgs a) {
         }
       }
     };
+    // ticks of step st: [first_tick(st), first_tick(st + 1)); the two extra ticks
+    // that drain the three-stage skew go to the first two steps
+    constexpr int kTps = 32 / kSteps;  // 1 at D = 128, 2 at D = 64
+    auto first_tick = [](int st) { return st * kTps + (st < 2 ? st : 2); };
+    // lane maximum of each half of sb[P]: eight max operations per half (a chain of
+    // 3-input maxima over its 16 values), from two products after the half's last S
+    // product, spread over the steps left
+    float mh[2];
+    auto max_op = [&](int half, int o) {
+      const f32x16& v = sb[P][half];
+      if (o == 0) mh[half] = __builtin_fmaxf(__builtin_fmaxf(v[0], v[1]), v[2]);
+      else if (o < 7) mh[half] = __builtin_fmaxf(__builtin_fmaxf(mh[half], v[2 * o + 1]), v[2 * o + 2]);
+      else mh[half] = __builtin_fmaxf(mh[half], v[15]);
+      pin(mh[half]);
+    };
+    auto max_step = [](int half, int o) {
+      const int start = kS.last_s[half] + 2;
+      const int avail = kSteps - start < 8 ? kSteps - start : 8;
+      return start + o * avail / 8;
+    };
     // this wave's K blocks, then its V blocks, at evenly spread products
     constexpr int kLoads = 2 * G::perWave;
     auto maybe_load = [&](auto stc) {
@@ -519,7 +566,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_sp(FwdArgs a) {
         }
       });
     };
-    constexpr int kTicksPerStep = 32 / kSteps;  // 1 at D = 128, 2 at D = 64
     // The two waves of a SIMD run the same stream at the same time; the issue
     // arbiter favours the older one (waves 0-3), which would finish its products
     // early and wait at the barrier while the other runs alone. Waves 4-7 get the
@@ -533,28 +579,28 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_sp(FwdArgs a) {
         asm volatile("s_setprio 1\n\ts_cmp_lt_u32 %0, 4\n\ts_cbranch_scc1 .Lprio_b%=\n\ts_setprio 0\n.Lprio_b%=:" ::"s"(wave)
                      : "scc");
       }
-      constexpr bool is_s = step_is_s_n<G::nS>(st);
-      constexpr int j = step_index_n<G::nS>(st);
-      if constexpr (is_s) {
-        if constexpr (j + kLook < G::nS) kop[(j + kLook) % (kLook + 1)] = k_read(kx, j + kLook);
-      } else {
-        if constexpr (j + kLook < G::nP) vop[(j + kLook) % (kLook + 1)] = v_read(vx0, vx1, j + kLook);
-      }
+      if constexpr (st + 2 < kSteps) op[(st + 2) % 3] = operand(std::integral_constant<int, st + 2>{});
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (is_s) {
-        constexpr int half = j / kHalfSteps, kk = j % kHalfSteps;
-        sb[P][half] = mfma32<FP16>(kop[j % (kLook + 1)], qreg[kk], kk == 0 ? f32x16{} : sb[P][half]);
+      if constexpr (kS.is_s[st]) {
+        constexpr int j = kS.idx[st];
+        constexpr int half = j / (D / 16), kk = j % (D / 16);
+        sb[P][half] = mfma32<FP16>(op[st % 3], qreg[kk], kk == 0 ? f32x16{} : sb[P][half]);
       } else {
+        constexpr int j = kS.idx[st];
         constexpr int t = j / (D / 32), db = j % (D / 32);
-        acc[db] = mfma32<FP16>(vop[j % (kLook + 1)], pb[P][t], acc[db]);
+        acc[db] = mfma32<FP16>(op[st % 3], pb[P][t], acc[db]);
       }
-      static_for<kTicksPerStep>([&](auto qc) { tick(std::integral_constant<int, st * kTicksPerStep + decltype(qc)::value>{}); });
+      static_for<first_tick(st + 1) - first_tick(st)>(
+          [&](auto qc) { tick(std::integral_constant<int, first_tick(st) + decltype(qc)::value>{}); });
+      static_for<16>([&](auto oc) {
+        constexpr int half = decltype(oc)::value / 8, o = decltype(oc)::value % 8;
+        if constexpr (max_step(half, o) == st) max_op(half, o);
+      });
       maybe_load(stc);
       __builtin_amdgcn_sched_barrier(0);
     });
-    tick(std::integral_constant<int, 32>{});
-    tick(std::integral_constant<int, 33>{});
     __builtin_amdgcn_s_setprio(0);
+    lmx = __builtin_fmaxf(mh[0], mh[1]);
     return sum;
   };
 
@@ -656,6 +702,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_sp(FwdArgs a) {
   // load and reading Q (once per item) come after the barrier.
   // Steady iterations (every wave computes all three slots, no mask, no item
   // boundary, no epilogue, not an item's first two tiles) skip the slot logic.
+  // lane maximum of the scores the last block computed (before any mask)
+  float lmx_blk = -INFINITY;
   bool pl_stop = false, pl_do_m = false, pl_do_s = false, pl_do_p = false, pl_first = false, pl_exact = false;
   bool pl_need_q = false, pl_q_issue = false, pl_q_keep = false;
   float pl_ref = INFINITY, pl_m = -INFINITY, pl_alpha = 1.0f;
@@ -697,8 +745,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_sp(FwdArgs a) {
     float ref = INFINITY, m_new = m_run, alpha = 1.0f;
     bool exact_m = false;
     if (do_m) {
-      if (mask_m) apply_mask(ic<Q>{}, m_t * kBN, c_q0);
-      const float lmx = lane_max(ic<Q>{});
+      float lmx = lmx_blk;
+      if (mask_m) {
+        apply_mask(ic<Q>{}, m_t * kBN, c_q0);
+        lmx = lane_max(ic<Q>{});
+      }
       exact_m = first || __any(lmx * sc > m_run + kSlack);
       if (exact_m) {
         const float mx = __builtin_fmaxf(lmx, other_half(lmx)) * sc;
@@ -750,7 +801,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_sp(FwdArgs a) {
     const __amdgpu_buffer_rsrc_t vr = ld_v ? cursor_rsrc(vc) : buffer_rsrc(a.v, 0);
     const bool q_keep = pl_q_keep;
     if (pl_do_s || pl_do_m || pl_do_p) {
-      const float sum = block(pc, pl_ref, kst, vst, kr, vr, kdst, vdst);
+      const float sum = block(pc, pl_ref, kst, vst, kr, vr, kdst, vdst, lmx_blk);
       if (pl_do_m) {
         l_run = pl_alpha * l_run + sum;
         m_run = pl_m;
@@ -813,32 +864,51 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_sp(FwdArgs a) {
   };
 
   // ---- steady runs ----
-  // Runs of steady iterations, two at a time (buffer parity 0 then 1), with the load
-  // descriptors advanced by a constant step and no slot logic: m-slot tiles t of the
-  // current item with 2 <= t and t + 1 <= min(last steady tile, n - 4), so that
-  // the loads (K three tiles ahead, V one) stay inside the item. The plan of each next
-  // iteration (reference choice from the lane maximum of the new scores) is taken
-  // before the barrier; the iteration after the run is planned in full.
-  auto steady_iter = [&](auto pc) {
+  // Runs of steady iterations, two at a time (buffer parity 0 then 1), without the
+  // slot logic: m-slot tiles t of the current item with 2 <= t <= n - 2 (the S slot
+  // stays in the item; tile 0 needs the exact maximum, tile 1's P V follows the
+  // previous item's epilogue). Every wave computes every slot. A tile that needs the
+  // mask (causal diagonal, ragged end) gets it before its lane maximum, and a tile
+  // wholly masked for a wave then gives it P = 0 by itself: its scores are all -inf,
+  // the reference stays at the (finite) running one and nothing is accumulated.
+  // The load cursors step without the item check while the K loads (three tiles
+  // ahead) stay in the item, t <= n - 4; the last iterations (K entering the next
+  // item) use the checked advance, and an exhausted stream loads an empty range as in
+  // the general iteration. The plan of each next iteration (mask, reference choice
+  // from the lane maximum of the new scores) is taken before the barrier; the
+  // iteration after the run is planned in full.
+  auto steady_iter = [&](auto pc, auto crossc) {
     constexpr int P = decltype(pc)::value;
+    constexpr bool kCross = decltype(crossc)::value;
     const int c3w = c3 == 0 ? 2 : c3 - 1;
     const int c3v = c3 == 2 ? 0 : c3 + 1;
-    const float sum = block(pc, pl_ref, c3 * G::tileBytes, G::vRing + c3v * G::tileBytes, cursor_rsrc(kc),
-                            cursor_rsrc(vc), kring + c3w * G::tileBytes, vring + c3 * G::tileBytes);
+    const bool ld_k = !kCross || kc.j >= 0, ld_v = !kCross || vc.j >= 0;
+    const __amdgpu_buffer_rsrc_t kr = ld_k ? cursor_rsrc(kc) : buffer_rsrc(a.k, 0);
+    const __amdgpu_buffer_rsrc_t vr = ld_v ? cursor_rsrc(vc) : buffer_rsrc(a.v, 0);
+    const float sum = block(pc, pl_ref, c3 * G::tileBytes, G::vRing + c3v * G::tileBytes, kr, vr,
+                            kring + c3w * G::tileBytes, vring + c3 * G::tileBytes, lmx_blk);
     l_run = pl_alpha * l_run + sum;
     m_run = pl_m;
     if (pl_exact) {
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) acc[db] *= pl_alpha;
     }
-    // inside a run both cursors stay in the item (the K cursor may step onto its end
-    // in the run's last iteration: fixed up after the run, before the next load)
-    cursor_step(kc);
-    cursor_step(vc);
+    if constexpr (kCross) {
+      if (ld_k) cursor_advance(kc, true);
+      if (ld_v) cursor_advance(vc, false);
+    } else {
+      cursor_step(kc);
+      cursor_step(vc);
+    }
     c3 = c3v;
     ++g;
-    // plan of the next iteration (steady: all slots, no mask): sb[P] holds its scores
-    const float lmx = lane_max(ic<P>{});
+    // plan of the next iteration (all slots): sb[P] holds its scores
+    const int mt = g - c_start;
+    float lmx = lmx_blk;
+    if (masked(c_q0, mt)) {
+      apply_mask(ic<P>{}, mt * kBN, c_q0);
+      lmx = lane_max(ic<P>{});
+    }
     pl_exact = __any(lmx * sc > m_run + kSlack);
     pl_m = m_run;
     pl_alpha = 1.0f;
@@ -853,18 +923,24 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_sp(FwdArgs a) {
   };
   auto steady_run = [&]() {
     const int t0 = g - c_start;
-    const int t_end = min(c_fl, c_n - 4);
-    if (!(c_j >= 0 && t0 >= 2 && t0 + 1 <= t_end)) return;
-    // the planned iteration is steady (no mask, not an item's first tile): pl_* hold
-    // its reference choice; the loads stay inside the item until the run ends
+    const int t_last = c_n - 2;
+    if (!(c_j >= 0 && t0 >= 2 && t0 + 1 <= t_last)) return;
+    // the planned iteration is steady (not an item's first two tiles): pl_* hold its
+    // reference choice
     int t = t0;
-    do {
-      steady_iter(ic<0>{});
-      steady_iter(ic<1>{});
+    const int t_step = c_n - 4;
+    while (t + 1 <= t_step) {
+      steady_iter(ic<0>{}, std::false_type{});
+      steady_iter(ic<1>{}, std::false_type{});
       t += 2;
-    } while (t + 1 <= t_end);
+    }
     cursor_settle(kc, true);
     cursor_settle(vc, false);
+    while (t + 1 <= t_last) {
+      steady_iter(ic<0>{}, std::true_type{});
+      steady_iter(ic<1>{}, std::true_type{});
+      t += 2;
+    }
     plan(ic<0>{});
   };
 
