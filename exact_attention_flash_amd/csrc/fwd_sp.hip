@@ -233,8 +233,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_sp(FwdArgs a) {
   // causal mask every SIMD has the same work on the diagonal tiles
   const int wave_rows = 32 * (wave < 4 ? wave : 11 - wave);
 
-  // ---- persistent schedule (items ranked heaviest causal query tile first, snake
-  // order over the workgroups, a slice's items on one XCD when B*H % 8 == 0) ----
+  // ---- persistent schedule (a group's slices in turn, each slice's query tiles
+  // heaviest causal tile first, dealt in snake order over the group's workgroups; a
+  // group is one XCD's share of the slices when B*H % 8 == 0, else all of them) ----
   const int bid = blockIdx.x;
   int wg_k, wg_n, hpx, bh_base;
   if (a.xcd_grouped) {
@@ -260,9 +261,30 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_sp(FwdArgs a) {
     const int j = r * wg_n + ((r & 1) ? wg_n - 1 - wg_k : wg_k);
     return j < n_items ? j : -1;
   };
-  auto grp_div = [&](int j) { return (int)fastdiv((uint32_t)j, a.grp_mul, a.grp_shift); };
-  auto item_bh = [&](int j) { return bh_base + j - grp_div(j) * hpx; };
-  auto item_q0 = [&](int j) { return (CAUSAL ? (a.q_tiles - 1 - grp_div(j)) : grp_div(j)) * kBM; };
+  // Item j of a schedule group. Slice-major order (slice j / q_tiles, query tile
+  // rank j % q_tiles): consecutive items -- those the group's workgroups run at the
+  // same time -- cover one or two slices, whose K/V tiles they then share through
+  // the XCD's L2. Under a causal mask the snake then gives each workgroup ranks i
+  // and q_tiles - 1 - i only when q_tiles divides twice the group's workgroups, so
+  // other causal shapes keep rank-major order (rank j / hpx, slice j % hpx: every
+  // slice's heaviest tiles first). Causal rank 0 is the last, heaviest tile.
+  const bool slice_major = a.slice_major != 0;
+  auto item_split = [&](int j, int& slice, int& rank) {
+    const int qd = (int)fastdiv((uint32_t)j, a.grp_mul, a.grp_shift);
+    const int rem = j - qd * (slice_major ? a.q_tiles : hpx);
+    slice = slice_major ? qd : rem;
+    rank = slice_major ? rem : qd;
+  };
+  auto item_bh = [&](int j) {
+    int slice, rank;
+    item_split(j, slice, rank);
+    return bh_base + slice;
+  };
+  auto item_q0 = [&](int j) {
+    int slice, rank;
+    item_split(j, slice, rank);
+    return (CAUSAL ? (a.q_tiles - 1 - rank) : rank) * kBM;
+  };
   auto item_tiles = [&](int q0) {
     return CAUSAL ? min(tiles_all, (min(q0 + kBM, N) - 1) / kBN + 1) : tiles_all;
   };
@@ -975,7 +997,10 @@ hipError_t launch_fwd_sp(const FwdArgs& args, bool fp16, int d, bool causal, hip
     if (grid < 8) grid = 8;
   }
   a.grid = grid;
-  const FastDiv grp = make_fastdiv((uint32_t)(a.xcd_grouped ? a.bh >> 3 : a.bh));
+  const int group_wgs = a.xcd_grouped ? grid >> 3 : grid;
+  a.slice_major = (!causal || (2 * group_wgs) % a.q_tiles == 0) ? 1 : 0;
+  const FastDiv grp =
+      make_fastdiv((uint32_t)(a.slice_major ? a.q_tiles : (a.xcd_grouped ? a.bh >> 3 : a.bh)));
   const FastDiv heads = make_fastdiv((uint32_t)a.heads);
   a.grp_mul = grp.mul;
   a.grp_shift = grp.shift;
