@@ -65,9 +65,10 @@
 // overflows. fp16 keeps r equal to the running row maximum (p <= 1). bf16 keeps
 // the reference of the previous tile and skips the row maximum: the tile's
 // probabilities are computed against it directly, and only if there is no
-// reference yet (first tile) or some partial row sum exceeds 2^64 (an exponent
-// argument past 64) is the tile redone with the exact running maximum. bf16 P
-// carries 8 bits at any magnitude, so probabilities up to 2^64 lose nothing.
+// reference yet (first tile) or some partial row sum exceeds 2^15 is the tile
+// redone with the exact running maximum. bf16 P carries 8 bits at any magnitude, so
+// probabilities up to 2^15 lose nothing, and the bound keeps the fp32 accumulator
+// finite for N * max|v| < 2^113 (the value range the interface states).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -90,7 +91,7 @@ constexpr int kStages = 3;        // LDS ring depth (tiles)
 constexpr int kAhead = kStages - 2;  // tiles in flight ahead of use
 
 // partial row sums above this send a bf16 tile back through the exact maximum
-constexpr float kBig = 0x1p64f;
+constexpr float kBig = 0x1p15f;
 
 // load offset of a masked head-dimension chunk: past every descriptor's range (the
 // host keeps slice extents below 2^31 bytes), so the load writes zeros to LDS

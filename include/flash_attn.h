@@ -83,6 +83,14 @@ typedef enum {
  *           the launch and never synchronises.
  * dtype   : FA_BF16 or FA_FP16.
  *
+ * Value range: with FA_BF16 a row's probabilities are taken relative to a kept
+ * reference that may lie up to 15 (log2 units) below the row's running maximum, so
+ * before normalisation they reach 2^15 and the fp32 accumulator sum_j p_j v_j stays
+ * finite only while N * max|v| < 2^113 (about 2.5e30 at N = 4096; bf16 itself reaches
+ * 3.4e38). Larger values can overflow to inf/NaN in o; they are not detected. With
+ * FA_FP16 the reference is the exact running maximum (p <= 1) and every fp16 value
+ * is admissible.
+ *
  * Ownership: the caller owns every buffer; the library allocates nothing, frees
  * nothing and keeps no pointer after returning. The library holds no state, so
  * concurrent calls on different streams are safe.
