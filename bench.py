@@ -25,7 +25,10 @@ flash_attn_fwd_strided at the headline shape with head dimensions 80 and 96 and
 with q, k, v taken from one packed [B, N, 3, H, d] tensor (FLOPs counted with the
 real d). --fp8 times the FP8 path at the headline shape: flash_attn_fwd_fp8 alone
 (the attention on quantized inputs; FLOPs as the metric counts them, against the
-5 PFLOP/s dense FP8 peak) and the three quantization calls.
+5 PFLOP/s dense FP8 peak) and the three quantization calls. --table prints one
+line per workload and mask: launch-time median, p10 and p90, TFLOP/s, % of peak,
+the recorded HBM bytes, and the oracle's time and parity metrics (max and mean abs
+error of O, excess over half an ulp, LSE error) on whole (batch, head) slices.
 """
 from __future__ import annotations
 
@@ -45,10 +48,15 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA, vendor figure
 PEAK_HBM_GBS = 8000.0
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense FP8 MFMA, vendor figure
-KERNEL_SOURCES = ["exact_attention_flash_amd/csrc/fwd_kernel.hip", "exact_attention_flash_amd/csrc/fwd_kernel.h",
+# sources of the kernel flash_attn_fwd launches (the software-pipelined forward)
+KERNEL_SOURCES = ["exact_attention_flash_amd/csrc/fwd_sp.hip", "exact_attention_flash_amd/csrc/fwd_kernel.h",
                   "exact_attention_flash_amd/csrc/gfx950_ops.h"]
+KERNEL_NAME = "fwd_sp (flash_attn_fwd)"
+# (batch, head) slices the oracle runs per workload in --table (all rows of each)
+TABLE_SLICES = {"single_head_n256_d64": 1, "mha_b4_h16_n1024_d64": 64, "llama7b_b2_h32_n4096_d128_causal": 8,
+                "longctx_b1_h32_n16384_d128_causal": 1, "stress_b3_h8_n4099_d128_sigma8": 6}
 BWD_FLOP_FACTOR = 2.5       # backward: S, dP, dV, dQ, dK products versus the forward's S and PV
-TRAFFIC_FILE = "profiles/fwd_kernel_hbm_traffic.txt"
+TRAFFIC_FILE = "profiles/fwd_sp_hbm_traffic.txt"
 
 
 def log(msg):
@@ -144,6 +152,9 @@ def time_gpu(w, causal, steps, warmup, bwd=False, splits=None):
     wall = time.perf_counter() - t0
     ev_ms = e0.elapsed_time(e1) / steps
     extra = torch.cuda.max_memory_allocated(dev) - mem0
+    gpu_out = None
+    if not bwd and splits is None:
+        gpu_out = (inputs.from_torch_bits(o), lse.double().cpu().numpy())
     return {
         "wall_s": wall, "ms_per_step": wall * 1e3 / steps, "event_ms_per_launch": ev_ms,
         "launch_ms_median": statistics.median(per_launch),
@@ -151,11 +162,25 @@ def time_gpu(w, causal, steps, warmup, bwd=False, splits=None):
         "launch_ms_p90": per_launch[int(0.9 * (len(per_launch) - 1))],
         "extra_alloc_bytes": int(extra),
         "device": torch.cuda.get_device_name(dev),
+        "gpu_out": gpu_out,
     }, (qb, kb, vb)
 
 
-def cpu_baseline(w, causal, qkv_bits, slices):
-    """Time the float64 oracle on `slices` complete (batch, head) slices of the workload."""
+def _half_ulp(x, dtype):
+    """Half the spacing of the 16-bit output type at |x| (subnormal spacing near 0)."""
+    import numpy as np
+
+    mant, min_exp = (7, -126) if dtype == "bf16" else (10, -14)
+    ax = np.abs(x)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(ax))
+    e = np.maximum(np.where(np.isfinite(e), e, min_exp), min_exp)
+    return np.ldexp(0.5, (e - mant).astype(np.int64))
+
+
+def cpu_baseline(w, causal, qkv_bits, slices, gpu_out=None):
+    """Time the float64 oracle on `slices` complete (batch, head) slices of the workload;
+    with the GPU's o (16-bit bits) and lse, also compare them on those slices."""
     import numpy as np
 
     from exact_attention_flash_amd import inputs
@@ -172,17 +197,29 @@ def cpu_baseline(w, causal, qkv_bits, slices):
     qb, kb, vb = (x.reshape(-1, w.N, w.d)[:slices] for x in qkv_bits)
     q, k, v = (inputs.bits_to_f64(x, w.dtype) for x in (qb, kb, vb))
     t0 = time.perf_counter()
-    attention(q, k, v, inputs.default_scale(w.d), causal=causal)
+    ro, rl = attention(q, k, v, inputs.default_scale(w.d), causal=causal)
     dt = time.perf_counter() - t0
     flops = 4.0 * slices * w.N * w.N * w.d / (2.0 if causal else 1.0)
-    _ = np
-    return {
+    out = {
         "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads or cores, "kind": "oracle",
         "sample": f"{slices} of {w.B * w.H} (batch, head) slices of the same workload, all {w.N} rows, "
                   f"float64 numpy (BLAS matmuls, {blas_threads} BLAS threads on {cores} host cores); "
                   f"{dt:.1f} s, scaled with the same FLOP formula",
         "seconds": dt,
     }
+    if gpu_out is not None:
+        ob, lse = gpu_out
+        o64 = inputs.bits_to_f64(ob.reshape(-1, w.N, w.d)[:slices], w.dtype)
+        l64 = lse.reshape(-1, w.N)[:slices]
+        err = np.abs(o64 - ro)
+        out["parity"] = {
+            "slices": slices,
+            "o_max_abs": float(err.max()),
+            "o_max_excess_over_half_ulp": float(np.maximum(err - _half_ulp(ro, w.dtype), 0.0).max()),
+            "o_mean_abs": float(err.mean()),
+            "lse_max_abs": float(np.abs(l64 - rl).max()),
+        }
+    return out
 
 
 def cpu_baseline_bwd(w, causal, qkv_bits, slices):
@@ -434,7 +471,7 @@ def run(args, workload_name, causal):
             "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": "fwd_kernel (flash_attn_fwd)",
+            "kernel": KERNEL_NAME,
             "flop_per_launch": flops,
             "launch_ms": round(g["event_ms_per_launch"], 5),
             "launch_ms_median": round(g["launch_ms_median"], 5),
@@ -447,8 +484,32 @@ def run(args, workload_name, causal):
         "kernel_source_sha256_16": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, causal, qkv, args.cpu_slices)
+        line["cpu_baseline"] = cpu_baseline(w, causal, qkv, args.cpu_slices, g["gpu_out"])
     return line
+
+
+def run_table(args):
+    """One line per workload and mask: launch-time distribution, TFLOP/s, % of peak,
+    recorded HBM bytes, and the oracle's time and parity metrics on whole slices."""
+    from exact_attention_flash_amd import inputs
+
+    for name, w in inputs.WORKLOADS.items():
+        for causal in w.causal:
+            g, qkv = time_gpu(w, causal, args.steps, args.warmup)
+            flops = w.flops(causal)
+            med = g["launch_ms_median"]
+            cb = cpu_baseline(w, causal, qkv, TABLE_SLICES[name], g["gpu_out"])
+            print(json.dumps({
+                "workload": name, "dtype": w.dtype, "causal": causal, "kernel": KERNEL_NAME,
+                "launch_ms_median": round(med, 5), "launch_ms_p10": round(g["launch_ms_p10"], 5),
+                "launch_ms_p90": round(g["launch_ms_p90"], 5),
+                "tflops_at_median": round(flops / (med * 1e-3) / 1e12, 2),
+                "pct_of_bf16_peak": round(100.0 * flops / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                "hbm_bytes_per_launch": measured_traffic(name, causal),
+                "compulsory_hbm_bytes": w.compulsory_bytes(),
+                "parity": cb["parity"], "oracle_seconds": round(cb["seconds"], 2), "oracle_cores": cb["cores"],
+                "kernel_source_sha256_16": kernel_source_hash(), "device": g["device"],
+                "steps": args.steps, "warmup": args.warmup}), flush=True)
 
 
 def main():
@@ -470,6 +531,9 @@ def main():
                     help="time the key-split forward against the plain one on underfilled shapes (diagnostic)")
     ap.add_argument("--cpu-bwd-slices", type=int, default=16,
                     help="(batch, head) slices the backward oracle times with --bwd")
+    ap.add_argument("--table", action="store_true",
+                    help="one line per workload and mask with timing distribution, recorded HBM bytes and "
+                         "oracle parity on whole slices (diagnostic)")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="only run plain device-to-device copies of MIB MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -488,6 +552,9 @@ def main():
 
     from exact_attention_flash_amd import inputs
 
+    if args.table:
+        run_table(args)
+        return
     if args.splitkv:
         run_splitkv(args)
         return
