@@ -28,12 +28,15 @@ bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p
 // the ping-pong kernel when FLASH_ATTN_FWD_KERNEL=pingpong (read once per process;
 // kept for comparisons). Calls with a key split always use the ping-pong kernel's
 // split instance.
+// d is the smallest instance width (64, 80, 96 or 128) that holds the real head
+// dimension; the ping-pong kernel has the 64- and 128-wide instances only.
 hipError_t launch_unsplit(const fa::FwdArgs& a, bool fp16, int d, bool causal, hipStream_t stream) {
   static const bool pingpong = [] {
     const char* e = std::getenv("FLASH_ATTN_FWD_KERNEL");
     return e != nullptr && std::strcmp(e, "pingpong") == 0;
   }();
-  return pingpong ? fa::launch_fwd(a, fp16, d, causal, stream) : fa::launch_fwd_sp(a, fp16, d, causal, stream);
+  return pingpong ? fa::launch_fwd(a, fp16, d <= 64 ? 64 : 128, causal, stream)
+                  : fa::launch_fwd_sp(a, fp16, d, causal, stream);
 }
 
 }  // namespace
@@ -337,7 +340,7 @@ extern "C" int flash_attn_fwd_strided(const void* q, const void* k, const void* 
   const int st = check_strided(q, k, v, o, lse, B, H, N, d, q_strides, k_strides, v_strides, o_strides,
                                lse_strides, causal, scale, dtype, &a, &empty);
   if (st != FA_OK || empty) return st;
-  const int inst = d <= 64 ? 64 : 128;
+  const int inst = d <= 64 ? 64 : d <= 80 ? 80 : d <= 96 ? 96 : 128;
   const hipError_t err =
       launch_unsplit(a, dtype == FA_FP16, inst, causal == 1, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? FA_OK : FA_ERR_HIP;

@@ -56,7 +56,8 @@ int device_cus();
 hipError_t launch_fwd(const FwdArgs& a, bool fp16, int d, bool causal, hipStream_t stream);
 
 // Enqueue the software-pipelined forward (no key split: a.splits must be 1) for
-// (dtype, d, causal); d is 64 or 128. Sizes the persistent grid like launch_fwd.
+// (dtype, d, causal); d is the instance width, 64, 80, 96 or 128 (a.d_real <= d
+// columns exist). Sizes the persistent grid like launch_fwd.
 hipError_t launch_fwd_sp(const FwdArgs& a, bool fp16, int d, bool causal, hipStream_t stream);
 
 }  // namespace fa

@@ -75,8 +75,6 @@ struct Geo {
   static constexpr int vRing = kStages * tileBytes;
   static constexpr int qRegion = 2 * kStages * tileBytes;
   static constexpr int ldsBytes = 2 * kStages * tileBytes + qBytes;
-  static constexpr int nS = D / 8;  // S products per tile (two 32-key halves, D/16 steps each)
-  static constexpr int nP = D / 8;  // P V products per tile (four 16-key chunks, D/32 blocks each)
   static_assert(blocksPerTile % kWaves == 0, "tile must split into whole 1 KiB blocks per wave");
   __device__ static __forceinline__ int swz(int row) { return chunk_swizzle<D>(row); }
 };
@@ -157,14 +155,15 @@ using ic = std::integral_constant<int, N>;
 // Order of the products in an iteration: S and P V alternate (S first); S products
 // take all 16-column steps of the first 32-key half before the second half, so the
 // first half of the new scores is complete halfway through.
-// Order of one block's products: D/8 S products (two 32-key halves of D/16 steps)
-// and D/8 P V products. The S products sit in a leading region with the P V products
-// spread evenly between them; the block ends with nP/2 - 1 P V products only, so that
-// both halves of the new scores are complete several products before the end and
-// their lane maxima are taken in the VALU slots of those last products.
-template <int D>
+// Order of one block's products: 2 KS S products (two 32-key halves of KS steps of 16
+// columns) and 4 NB P V products (four 16-key chunks of NB blocks of 32 output
+// columns). The S products sit in a leading region with the P V products spread
+// evenly between them; the block ends with nP/2 - 1 P V products only, so that both
+// halves of the new scores are complete several products before the end and their
+// lane maxima are taken in the VALU slots of those last products.
+template <int KS, int NB>
 struct Sched {
-  static constexpr int nS = D / 8, nP = D / 8, kSteps = nS + nP;
+  static constexpr int nS = 2 * KS, nP = 4 * NB, kSteps = nS + nP;
   static constexpr int tailP = nP / 2 - 1;
   static constexpr int region = kSteps - tailP;
   bool is_s[kSteps];
@@ -188,7 +187,8 @@ struct Sched {
     return ns == nS && np == nP && last_s[1] + 2 < kSteps && last_s[0] < last_s[1];
   }
 };
-static_assert(Sched<128>().valid() && Sched<64>().valid(), "block schedule");
+static_assert(Sched<8, 4>().valid() && Sched<6, 3>().valid() && Sched<5, 3>().valid() && Sched<4, 2>().valid(),
+              "block schedule");
 
 // f(integral_constant<int, i>) for i = 0 .. N-1, expanded at compile time (a loop
 // the unroller might leave rolled would index the register arrays dynamically)
@@ -218,7 +218,14 @@ __device__ __forceinline__ void pin(T& x) {
 
 template <bool FP16, int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void fwd_sp(FwdArgs a) {
-  using G = Geo<D>;
+  // LDS and load layout: rows of DL = 64 or 128 columns (a power-of-two chunk count
+  // for the swizzle, whole 1 KiB blocks per wave); arithmetic: KS = D/16 steps of 16
+  // columns per S half and NB = ceil(D/32) blocks of 32 output columns (D = 80 and 96
+  // skip the padding columns a 128-wide instance would multiply)
+  constexpr int DL = D <= 64 ? 64 : 128;
+  constexpr int KS = D / 16, NB = (D + 31) / 32;
+  static_assert(D % 16 == 0 && D <= DL, "head dimension of an instance");
+  using G = Geo<DL>;
   __shared__ __attribute__((aligned(1024))) char smem[G::ldsBytes];
   char* const kring = smem;
   char* const vring = smem + G::vRing;
@@ -399,12 +406,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_sp(FwdArgs a) {
     }
   };
   // every lane reads its query's row into the B operands (k-slots d = 16 kk + 8 h + 0..7)
-  u32x4 qreg[D / 16];
+  u32x4 qreg[KS];
   auto read_q = [&]() {
     int row = wave_rows + l32;
     asm volatile("" : "+v"(row));
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
+    for (int kk = 0; kk < KS; ++kk)
       qreg[kk] = lds_read16(qsm + row * G::rowBytes + (((2 * kk + h) ^ G::swz(row)) * 16));
   };
 
@@ -437,7 +444,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_sp(FwdArgs a) {
   constexpr float kSlack = FP16 ? 0.0f : 15.0f;
   f32x16 sb[2][2];    // S^T accumulators [buffer][32-key half]: lane = query, 16 keys each
   u32x4 pb[2][4];     // 16-bit P as B operands [buffer][16-key chunk]
-  f32x16 acc[D / 32];  // u^T: 32 columns of the head dimension per block
+  f32x16 acc[NB];  // u^T: 32 columns of the head dimension per block
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     sb[b][0] = sb[b][1] = f32x16{};
@@ -445,7 +452,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_sp(FwdArgs a) {
     for (int t = 0; t < 4; ++t) pb[b][t] = u32x4{};
   }
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
+  for (int db = 0; db < NB; ++db) acc[db] = f32x16{};
   float m_run = -INFINITY;  // reference (log2 units) of this lane's query
   float l_run = 0.f;        // denominator over this half-wave's keys
   // a finished item's statistics: x_* once the softmax leaves the item, e_* once its
@@ -459,7 +466,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_sp(FwdArgs a) {
   // operand reads: S product j covers 32-key half j / (D/16) and 16-column step
   // j % (D/16) (all steps of half 0 first, so that half's accumulator is complete
   // early); P V product j covers 16-key chunk j / (D/32) and 32-column block j % (D/32)
-  constexpr int kHalfSteps = D / 16;
+  constexpr int kHalfSteps = KS;
   // kx, vx0, vx1: this iteration's stage offsets (multiples of the tile size, so
   // above every bit the XOR touches) plus the lane bases
   auto k_read = [&](int kx, int j) {
@@ -467,7 +474,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_sp(FwdArgs a) {
     return lds_read16(smem + ((kx ^ (32 * kk)) + half * 32 * G::rowBytes));
   };
   auto v_read = [&](int vx0, int vx1, int j) {
-    const int t = j / (D / 32), db = j % (D / 32);
+    const int t = j / NB, db = j % NB;
     const u32x2 lo = lds_read_tr16(smem + ((vx0 ^ (64 * db)) + 16 * t * G::rowBytes));
     const u32x2 hi = lds_read_tr16(smem + ((vx1 ^ (64 * db)) + 16 * t * G::rowBytes));
     return u32x4{lo[0], lo[1], hi[0], hi[1]};
@@ -504,15 +511,15 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_sp(FwdArgs a) {
   // unrounded fp32 probabilities), u += V^T P^T from pb[P], the lane maximum of the
   // new scores sb[P] (unmasked, unscaled) into `lmx`, and this wave's share of the
   // tile loads (K_{g+3} from descriptor kr into kdst, V_{g+1} from vr into vdst).
-  // Products follow Sched<D>; each carries one score's softmax work (two at D = 64),
+  // Products follow Sched<KS, NB>; each carries one score's softmax work (two at D = 64),
   // split into three stages two ticks apart so that no instruction waits on the one
   // before it; the operand of each product is read two products ahead.
   auto block = [&](auto pc, float ref, int kst, int vst, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
                    char* kdst, char* vdst, float& lmx) {
     constexpr int P = decltype(pc)::value;
     constexpr int Q = P ^ 1;
-    constexpr Sched<D> kS{};
-    constexpr int kSteps = Sched<D>::kSteps;
+    constexpr Sched<KS, NB> kS{};
+    constexpr int kSteps = Sched<KS, NB>::kSteps;
     const int kx = kst + kbase, vx0 = vst + vbase[0], vx1 = vst + vbase[1];
     auto operand = [&](auto stc) -> u32x4 {
       constexpr int st = decltype(stc)::value;
@@ -552,10 +559,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_sp(FwdArgs a) {
         }
       }
     };
-    // ticks of step st: [first_tick(st), first_tick(st + 1)); the two extra ticks
-    // that drain the three-stage skew go to the first two steps
-    constexpr int kTps = 32 / kSteps;  // 1 at D = 128, 2 at D = 64
-    auto first_tick = [](int st) { return st * kTps + (st < 2 ? st : 2); };
+    // ticks of step st: [first_tick(st), first_tick(st + 1)). With 32 / kSteps whole
+    // (D = 128: 1, D = 64: 2) the two extra ticks that drain the three-stage skew go to
+    // the first two steps; otherwise the 34 ticks are spread evenly.
+    constexpr int kTps = 32 / kSteps;
+    auto first_tick = [](int st) {
+      if (32 % kSteps == 0) return st * kTps + (st < 2 ? st : 2);
+      return st * 34 / kSteps;
+    };
     // lane maximum of each half of sb[P]: eight max operations per half (a chain of
     // 3-input maxima over its 16 values), from two products after the half's last S
     // product, spread over the steps left
@@ -605,11 +616,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_sp(FwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (kS.is_s[st]) {
         constexpr int j = kS.idx[st];
-        constexpr int half = j / (D / 16), kk = j % (D / 16);
+        constexpr int half = j / KS, kk = j % KS;
         sb[P][half] = mfma32<FP16>(op[st % 3], qreg[kk], kk == 0 ? f32x16{} : sb[P][half]);
       } else {
         constexpr int j = kS.idx[st];
-        constexpr int t = j / (D / 32), db = j % (D / 32);
+        constexpr int t = j / NB, db = j % NB;
         acc[db] = mfma32<FP16>(op[st % 3], pb[P][t], acc[db]);
       }
       static_for<first_tick(st + 1) - first_tick(st)>(
@@ -634,9 +645,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_sp(FwdArgs a) {
     // a lane holds four columns of each group of eight and the lane 32 away the other
     // four of the same row: one swap gives the lower half all eight columns of an even
     // group and the upper half all eight of the odd group after it
-    u32x4 w[D / 16];
+    u32x4 w[2 * NB];
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < NB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; g += 2) {
         const uint32_t e0 = pack2<FP16>(acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv);
@@ -652,16 +663,16 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_sp(FwdArgs a) {
       const int d_real = ka->d_real;
       uint16_t* og =
           reinterpret_cast<uint16_t*>(ka->o) + slice_off(bh, ka->o_sb, ka->o_sh) + (int64_t)qrow * ka->o_sn + 8 * h;
-      if (d_real == D) {
+      if (d_real == 32 * NB) {
 #pragma unroll
-        for (int k = 0; k < D / 16; ++k) *reinterpret_cast<u32x4*>(og + 16 * k) = w[k];
+        for (int k = 0; k < 2 * NB; ++k) *reinterpret_cast<u32x4*>(og + 16 * k) = w[k];
       } else {
         // d_real is a multiple of 8: each piece is wholly inside or outside (the lane's
         // column offset is recomputed here rather than kept per piece across the loop)
         int c8 = 8 * h;
         asm volatile("" : "+v"(c8));
 #pragma unroll
-        for (int k = 0; k < D / 16; ++k)
+        for (int k = 0; k < 2 * NB; ++k)
           if (c8 < d_real - 16 * k) *reinterpret_cast<u32x4*>(og + 16 * k) = w[k];
       }
       if (h == 0)
@@ -669,7 +680,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_sp(FwdArgs a) {
             (e_m + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994530942f;
     }
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
+    for (int db = 0; db < NB; ++db) acc[db] = f32x16{};
   };
 
   // ---- the compute slots' items: cur holds tile g (the first item before g = 0),
@@ -831,7 +842,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_sp(FwdArgs a) {
         // tile u belongs to the previous item, awaiting its epilogue)
         if (pl_exact && !pl_first) {
 #pragma unroll
-          for (int db = 0; db < D / 32; ++db) acc[db] *= pl_alpha;
+          for (int db = 0; db < NB; ++db) acc[db] *= pl_alpha;
         }
       }
     } else {
@@ -913,7 +924,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_sp(FwdArgs a) {
     m_run = pl_m;
     if (pl_exact) {
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) acc[db] *= pl_alpha;
+      for (int db = 0; db < NB; ++db) acc[db] *= pl_alpha;
     }
     if constexpr (kCross) {
       if (ld_k) cursor_advance(kc, true);
@@ -1006,12 +1017,17 @@ hipError_t launch_fwd_sp(const FwdArgs& args, bool fp16, int d, bool causal, hip
   a.grp_shift = grp.shift;
   a.heads_mul = heads.mul;
   a.heads_shift = heads.shift;
-  if (fp16) {
-    if (d == 64) return causal ? launch_one<true, 64, true>(a, stream) : launch_one<true, 64, false>(a, stream);
-    return causal ? launch_one<true, 128, true>(a, stream) : launch_one<true, 128, false>(a, stream);
-  }
-  if (d == 64) return causal ? launch_one<false, 64, true>(a, stream) : launch_one<false, 64, false>(a, stream);
-  return causal ? launch_one<false, 128, true>(a, stream) : launch_one<false, 128, false>(a, stream);
+  auto pick = [&](auto fp16c) -> hipError_t {
+    constexpr bool F = decltype(fp16c)::value;
+    switch (d) {
+      case 64: return causal ? launch_one<F, 64, true>(a, stream) : launch_one<F, 64, false>(a, stream);
+      case 80: return causal ? launch_one<F, 80, true>(a, stream) : launch_one<F, 80, false>(a, stream);
+      case 96: return causal ? launch_one<F, 96, true>(a, stream) : launch_one<F, 96, false>(a, stream);
+      case 128: return causal ? launch_one<F, 128, true>(a, stream) : launch_one<F, 128, false>(a, stream);
+      default: return hipErrorInvalidValue;
+    }
+  };
+  return fp16 ? pick(std::true_type{}) : pick(std::false_type{});
 }
 
 }  // namespace fa

@@ -121,8 +121,8 @@ int flash_attn_fwd_validate(const void* q, const void* k, const void* v, void* o
  * per batch, head and row for each of q, k, v, o; batch and head strides for the
  * row statistics), and a head dimension that is not a power of two is handled as
  * that section handles BLOCK_D > D: the kernel works on the next size it is built
- * for (64 or 128) with the positions past d masked, so they add nothing to the
- * scores and are never stored.
+ * for (64, 80, 96 or 128) with the positions past d masked, so they add nothing to
+ * the scores and are never stored.
  *
  * Element (b, h, i, c) of q is q[b*q_strides[0] + h*q_strides[1] + i*q_strides[2] + c]
  * (in elements of `dtype`; the head dimension is contiguous), likewise k, v and o;

@@ -62,7 +62,7 @@ def _oracle(bits, dtype, causal, scale):
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("dtype", [inputs.BF16, inputs.FP16])
-@pytest.mark.parametrize("d", [8, 24, 40, 56, 72, 80, 96, 120])
+@pytest.mark.parametrize("d", [8, 24, 40, 56, 72, 80, 88, 96, 120])
 def test_head_dims(fa, d, dtype, causal):
     shape = (2, 2, 300, d)
     scale = _scale(d)
@@ -158,6 +158,24 @@ def test_contiguous_strided_equals_plain(fa, d, causal):
     fa.flash_attn_fwd_strided(q, k, v, o2, l2, causal=causal, scale=0.1)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [80, 96])
+def test_head_dims_multi_item_workgroups(fa, d, causal):
+    """The 80- and 96-wide instances with several items per workgroup (4*32 slices of
+    three 256-row query tiles, the last ragged: 384 items on at most 256 workgroups),
+    compared in full."""
+    shape, dtype = (4, 32, 600, d), inputs.BF16
+    scale = _scale(d)
+    bits = inputs.draw_qkv(shape, dtype, 1.0, 800 + d + (1 if causal else 0))
+    q, k, v = (_dev_from_bits(x, dtype) for x in bits)
+    o, lse = fa.forward(q, k, v, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    ro, rl = _oracle(bits, dtype, causal, scale)
+    m = metrics(_o64(o, dtype), lse.double().cpu().numpy(), ro, rl, dtype)
+    _log(f"strided d={d} multi-item causal={causal}: {m}")
+    assert_parity(m, f"d={d} multi-item causal={causal}")
 
 
 def test_workload_shape_d80(fa):
