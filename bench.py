@@ -24,8 +24,8 @@ planned for this GPU) on the shapes that underfill it. --strided times
 flash_attn_fwd_strided at the headline shape with head dimensions 80 and 96 and
 with q, k, v taken from one packed [B, N, 3, H, d] tensor (FLOPs counted with the
 real d). --fp8 times the FP8 path at the headline shape: flash_attn_fwd_fp8 alone
-(the attention on quantized inputs; FLOPs as the metric counts them, against the
-5 PFLOP/s dense FP8 peak) and the three quantization calls. --table prints one
+(the attention on quantized inputs, E4M3 and E5M2; FLOPs as the metric counts them,
+against the 5 PFLOP/s dense FP8 peak) and the three quantization calls. --table prints one
 line per workload and mask: launch-time median, p10 and p90, TFLOP/s, % of peak,
 the recorded HBM bytes, and the oracle's time and parity metrics (max and mean abs
 error of O, excess over half an ulp, LSE error) on whole (batch, head) slices.
@@ -413,33 +413,36 @@ def run_fp8(args):
     q, k, v = (inputs.to_torch(x, w.dtype, dev) for x in (qb, kb, vb))
     stream = torch.cuda.current_stream(dev)
     scale = inputs.default_scale(w.d)
-    q8, qs = fa.quantize_fp8(q)
-    k8, ks = fa.quantize_fp8(k)
-    v8, vs = fa.quantize_fp8(v, keys_transposed=True)
-    o = torch.empty_like(q)
-    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
-    attn = lambda: fa.flash_attn_fwd_fp8(q8, k8, v8, qs, ks, vs, o, lse, causal=True, scale=scale, stream=stream)
+    for fmt in ("e4m3", "e5m2"):
+        q8, qs = fa.quantize_fp8(q, fmt=fmt)
+        k8, ks = fa.quantize_fp8(k, fmt=fmt)
+        v8, vs = fa.quantize_fp8(v, keys_transposed=True, fmt=fmt)
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
 
-    def quant():
-        fa.quantize_fp8(q, stream=stream)
-        fa.quantize_fp8(k, stream=stream)
-        fa.quantize_fp8(v, keys_transposed=True, stream=stream)
+        def attn():
+            fa.flash_attn_fwd_fp8(q8, k8, v8, qs, ks, vs, o, lse, causal=True, scale=scale, stream=stream, fmt=fmt)
 
-    ms, med = _time_calls(attn, args.steps, args.warmup, stream)
-    qms, _ = _time_calls(quant, max(10, args.steps // 4), args.warmup, stream)
-    flops = w.flops(True)
-    tf = flops / (ms * 1e-3) / 1e12
-    in_bytes = 3 * w.B * w.H * w.N * w.d * 2
-    print(json.dumps({
-        "metric": "attention fwd TFLOP/s on FP8 inputs (diagnostic)",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": True,
-                   "inputs": "E4M3, power-of-two scale per 64 rows", "out_dtype": w.dtype},
-        "value": round(tf, 2), "unit": "TFLOP/s", "launch_ms": round(ms, 5), "launch_ms_median": round(med, 5),
-        "pct_of_fp8_peak": round(100 * tf / PEAK_FP8_TFLOPS, 2),
-        "pct_of_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
-        "quantize_q_k_v_ms": round(qms, 5),
-        "quantize_GB_per_s": round((in_bytes + in_bytes / 2) / (qms * 1e-3) / 1e9, 1),
-        "steps": args.steps, "warmup": args.warmup}), flush=True)
+        def quant():
+            fa.quantize_fp8(q, stream=stream, fmt=fmt)
+            fa.quantize_fp8(k, stream=stream, fmt=fmt)
+            fa.quantize_fp8(v, keys_transposed=True, stream=stream, fmt=fmt)
+
+        ms, med = _time_calls(attn, args.steps, args.warmup, stream)
+        qms, _ = _time_calls(quant, max(10, args.steps // 4), args.warmup, stream)
+        flops = w.flops(True)
+        tf = flops / (ms * 1e-3) / 1e12
+        in_bytes = 3 * w.B * w.H * w.N * w.d * 2
+        print(json.dumps({
+            "metric": "attention fwd TFLOP/s on FP8 inputs (diagnostic)",
+            "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": True,
+                       "inputs": f"{fmt.upper()}, power-of-two scale per 64 rows", "out_dtype": w.dtype},
+            "value": round(tf, 2), "unit": "TFLOP/s", "launch_ms": round(ms, 5), "launch_ms_median": round(med, 5),
+            "pct_of_fp8_peak": round(100 * tf / PEAK_FP8_TFLOPS, 2),
+            "pct_of_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+            "quantize_q_k_v_ms": round(qms, 5),
+            "quantize_GB_per_s": round((in_bytes + in_bytes / 2) / (qms * 1e-3) / 1e9, 1),
+            "steps": args.steps, "warmup": args.warmup}), flush=True)
 
 
 def run(args, workload_name, causal):

@@ -13,7 +13,7 @@ from . import _native
 from ._native import (FA_BF16, FA_FP16, FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEADDIM,  # noqa: F401
                       FA_ERR_DTYPE, FA_ERR_SCALE, FA_ERR_ALIGN, FA_ERR_ALIAS, FA_ERR_HIP, FA_ERR_ARG,
                       FA_ERR_WORKSPACE, FA_ERR_STRIDE, FA_ERR_SCRATCH, FA_SPLITKV_SCRATCH_BYTES,
-                      FA_FP8_ROWS, FA_FP8_KEYS_T)
+                      FA_FP8_ROWS, FA_FP8_KEYS_T, FA_FP8_E4M3, FA_FP8_E5M2)
 
 __all__ = ["forward", "backward", "forward_splitkv", "flash_attn_fwd", "flash_attn_fwd_strided",
            "flash_attn_fwd_splitkv", "flash_attn_fwd_splitkv_noalloc", "flash_attn_bwd",
@@ -281,8 +281,18 @@ def backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = 
     return dq, dk, dv
 
 
-def quantize_fp8(x, keys_transposed: bool = False, stream=None):
-    """Block-quantize a contiguous [B, H, N, d] bf16/fp16 CUDA tensor to E4M3.
+_FP8_FORMATS = {"e4m3": FA_FP8_E4M3, "e5m2": FA_FP8_E5M2}
+
+
+def _fp8_format(fmt: str) -> int:
+    if fmt not in _FP8_FORMATS:
+        raise ValueError(f"fp8 format must be one of {sorted(_FP8_FORMATS)}, not {fmt!r}")
+    return _FP8_FORMATS[fmt]
+
+
+def quantize_fp8(x, keys_transposed: bool = False, stream=None, fmt: str = "e4m3"):
+    """Block-quantize a contiguous [B, H, N, d] bf16/fp16 CUDA tensor to FP8 (fmt "e4m3"
+    or "e5m2").
 
     Returns (x8, scale_codes): x8 is uint8 [B, H, N, d] (rows layout) or
     [B, H, ceil(N/64), d, 64] (keys-transposed layout, for values); scale_codes is
@@ -300,16 +310,17 @@ def quantize_fp8(x, keys_transposed: bool = False, stream=None):
     if stream is None:
         stream = torch.cuda.current_stream(x.device)
     st = _native.quantize_raw(x.data_ptr(), x8.data_ptr(), se.data_ptr(), B, H, N, d,
-                              FA_FP8_KEYS_T if keys_transposed else FA_FP8_ROWS, stream.cuda_stream, _dtype_code(x))
+                              FA_FP8_KEYS_T if keys_transposed else FA_FP8_ROWS, stream.cuda_stream, _dtype_code(x),
+                              _fp8_format(fmt))
     if st != FA_OK:
         raise FlashAttnError(st, "flash_attn_quantize_fp8")
     return x8, se
 
 
 def flash_attn_fwd_fp8(q8, k8, v8t, q_scale, k_scale, v_scale, o, lse, causal: bool = False,
-                       scale: float | None = None, stream=None) -> None:
-    """The FP8 forward on caller-owned tensors (outputs of quantize_fp8; o [B, H, N, 128]
-    bf16/fp16 and lse [B, H, N] float32)."""
+                       scale: float | None = None, stream=None, fmt: str = "e4m3") -> None:
+    """The FP8 forward on caller-owned tensors (outputs of quantize_fp8 in format fmt;
+    o [B, H, N, 128] bf16/fp16 and lse [B, H, N] float32)."""
     import torch
 
     B, H, N, d = o.shape
@@ -325,22 +336,22 @@ def flash_attn_fwd_fp8(q8, k8, v8t, q_scale, k_scale, v_scale, o, lse, causal: b
         stream = torch.cuda.current_stream(o.device)
     st = _native.fp8_raw(q8.data_ptr(), k8.data_ptr(), v8t.data_ptr(), q_scale.data_ptr(), k_scale.data_ptr(),
                          v_scale.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, d, causal, scale,
-                         stream.cuda_stream, _dtype_code(o))
+                         stream.cuda_stream, _dtype_code(o), _fp8_format(fmt))
     if st != FA_OK:
         raise FlashAttnError(st, "flash_attn_fwd_fp8")
 
 
-def forward_fp8(q, k, v, causal: bool = False, scale: float | None = None, stream=None):
-    """Quantize q, k, v to E4M3 (64-row blocks) and run the FP8 forward; o has q's dtype.
-    Returns (o, lse)."""
+def forward_fp8(q, k, v, causal: bool = False, scale: float | None = None, stream=None, fmt: str = "e4m3"):
+    """Quantize q, k, v to FP8 (fmt "e4m3" or "e5m2", 64-row blocks) and run the FP8
+    forward; o has q's dtype. Returns (o, lse)."""
     import torch
 
-    q8, qs = quantize_fp8(q, stream=stream)
-    k8, ks = quantize_fp8(k, stream=stream)
-    v8, vs = quantize_fp8(v, keys_transposed=True, stream=stream)
+    q8, qs = quantize_fp8(q, stream=stream, fmt=fmt)
+    k8, ks = quantize_fp8(k, stream=stream, fmt=fmt)
+    v8, vs = quantize_fp8(v, keys_transposed=True, stream=stream, fmt=fmt)
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
-    flash_attn_fwd_fp8(q8, k8, v8, qs, ks, vs, o, lse, causal=causal, scale=scale, stream=stream)
+    flash_attn_fwd_fp8(q8, k8, v8, qs, ks, vs, o, lse, causal=causal, scale=scale, stream=stream, fmt=fmt)
     return o, lse
 
 

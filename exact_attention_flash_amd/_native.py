@@ -28,6 +28,8 @@ FA_SPLITKV_SCRATCH_BYTES = 65 * 1024 * 1024
 
 FA_FP8_ROWS = 0
 FA_FP8_KEYS_T = 1
+FA_FP8_E4M3 = 0
+FA_FP8_E5M2 = 1
 
 _lib = None
 
@@ -60,12 +62,13 @@ def lib() -> ctypes.CDLL:
         L.flash_attn_fwd_strided_validate.argtypes = L.flash_attn_fwd_strided.argtypes
         vp = ctypes.c_void_p
         L.flash_attn_quantize_fp8.restype = ctypes.c_int
-        L.flash_attn_quantize_fp8.argtypes = [vp, vp, vp] + [ctypes.c_int64] * 4 + [ctypes.c_int, vp, ctypes.c_int]
+        L.flash_attn_quantize_fp8.argtypes = [vp, vp, vp] + [ctypes.c_int64] * 4 + [ctypes.c_int, vp, ctypes.c_int,
+                                                                              ctypes.c_int]
         L.flash_attn_quantize_fp8_validate.restype = ctypes.c_int
         L.flash_attn_quantize_fp8_validate.argtypes = L.flash_attn_quantize_fp8.argtypes
         L.flash_attn_fwd_fp8.restype = ctypes.c_int
         L.flash_attn_fwd_fp8.argtypes = [vp] * 8 + [ctypes.c_int64] * 4 + [ctypes.c_int, ctypes.c_float, vp,
-                                                                          ctypes.c_int]
+                                                                          ctypes.c_int, ctypes.c_int]
         L.flash_attn_fwd_fp8_validate.restype = ctypes.c_int
         L.flash_attn_fwd_fp8_validate.argtypes = L.flash_attn_fwd_fp8.argtypes
         L.flash_attn_fwd_splitkv.restype = ctypes.c_int
@@ -134,22 +137,23 @@ def validate_strided_raw(q, k, v, o, lse, B, H, N, d, qs, ks, vs, os_, ls, causa
                                                  float(scale), stream, dtype)
 
 
-def quantize_raw(x, x8, se, B, H, N, d, layout, stream, dtype) -> int:
-    return lib().flash_attn_quantize_fp8(x, x8, se, B, H, N, d, int(layout), stream, dtype)
+def quantize_raw(x, x8, se, B, H, N, d, layout, stream, dtype, fmt=FA_FP8_E4M3) -> int:
+    return lib().flash_attn_quantize_fp8(x, x8, se, B, H, N, d, int(layout), stream, dtype, int(fmt))
 
 
-def validate_quantize_raw(x, x8, se, B, H, N, d, layout, stream, dtype) -> int:
-    return lib().flash_attn_quantize_fp8_validate(x, x8, se, B, H, N, d, int(layout), stream, dtype)
+def validate_quantize_raw(x, x8, se, B, H, N, d, layout, stream, dtype, fmt=FA_FP8_E4M3) -> int:
+    return lib().flash_attn_quantize_fp8_validate(x, x8, se, B, H, N, d, int(layout), stream, dtype, int(fmt))
 
 
-def fp8_raw(q8, k8, v8t, qs, ks, vs, o, lse, B, H, N, d, causal, scale, stream, out_dtype) -> int:
+def fp8_raw(q8, k8, v8t, qs, ks, vs, o, lse, B, H, N, d, causal, scale, stream, out_dtype, fmt=FA_FP8_E4M3) -> int:
     return lib().flash_attn_fwd_fp8(q8, k8, v8t, qs, ks, vs, o, lse, B, H, N, d, int(causal), float(scale), stream,
-                                    out_dtype)
+                                    out_dtype, int(fmt))
 
 
-def validate_fp8_raw(q8, k8, v8t, qs, ks, vs, o, lse, B, H, N, d, causal, scale, stream, out_dtype) -> int:
+def validate_fp8_raw(q8, k8, v8t, qs, ks, vs, o, lse, B, H, N, d, causal, scale, stream, out_dtype,
+                     fmt=FA_FP8_E4M3) -> int:
     return lib().flash_attn_fwd_fp8_validate(q8, k8, v8t, qs, ks, vs, o, lse, B, H, N, d, int(causal),
-                                             float(scale), stream, out_dtype)
+                                             float(scale), stream, out_dtype, int(fmt))
 
 
 def splitkv_raw(q, k, v, o, lse, B, H, N, d, causal, scale, num_splits, ws, ws_bytes, stream, dtype) -> int:

@@ -41,7 +41,7 @@ hipError_t launch_unsplit(const fa::FwdArgs& a, bool fp16, int d, bool causal, h
 
 }  // namespace
 
-extern "C" int flash_attn_abi_version(void) { return 6; }
+extern "C" int flash_attn_abi_version(void) { return 7; }
 
 extern "C" const char* flash_attn_strerror(int status) {
   switch (status) {
@@ -54,7 +54,7 @@ extern "C" const char* flash_attn_strerror(int status) {
     case FA_ERR_ALIGN: return "16-bit tensors must be 16-byte aligned and fp32 ones 4-byte aligned";
     case FA_ERR_ALIAS: return "an output overlaps an input or another output";
     case FA_ERR_HIP: return "HIP runtime error at launch";
-    case FA_ERR_ARG: return "causal must be 0 or 1, and num_splits >= 0";
+    case FA_ERR_ARG: return "causal must be 0 or 1, num_splits >= 0, and an FP8 layout or format one of those defined";
     case FA_ERR_WORKSPACE: return "workspace is NULL, misaligned or smaller than the split needs";
     case FA_ERR_STRIDE:
       return "a stride is negative, not a multiple of 8 elements, a row stride is below d or too large, a slice "
@@ -415,12 +415,13 @@ extern "C" int flash_attn_fwd_splitkv(const void* q, const void* k, const void* 
 namespace {
 
 int check_quant(const void* x, void* x8, int32_t* se, int64_t B, int64_t H, int64_t N, int64_t d, int layout,
-                int dtype, fa::QuantArgs* a, bool* empty) {
+                int dtype, int format, fa::QuantArgs* a, bool* empty) {
   *empty = false;
   if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_HEADDIM;
   if (dtype != FA_BF16 && dtype != FA_FP16) return FA_ERR_DTYPE;
   if (layout != FA_FP8_ROWS && layout != FA_FP8_KEYS_T) return FA_ERR_ARG;
+  if (format != FA_FP8_E4M3 && format != FA_FP8_E5M2) return FA_ERR_ARG;
   if (B == 0 || H == 0 || N == 0) {
     *empty = true;
     return FA_OK;
@@ -446,12 +447,13 @@ int check_quant(const void* x, void* x8, int32_t* se, int64_t B, int64_t H, int6
 
 int check_fp8(const void* q8, const void* k8, const void* v8t, const int32_t* qs, const int32_t* ks,
               const int32_t* vs, void* o, float* lse, int64_t B, int64_t H, int64_t N, int64_t d, int causal,
-              float scale, int out_dtype, fa::Fp8Args* a, bool* empty) {
+              float scale, int out_dtype, int format, fa::Fp8Args* a, bool* empty) {
   *empty = false;
   if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
   if (d != 128) return FA_ERR_HEADDIM;
   if (out_dtype != FA_BF16 && out_dtype != FA_FP16) return FA_ERR_DTYPE;
   if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  if (format != FA_FP8_E4M3 && format != FA_FP8_E5M2) return FA_ERR_ARG;
   if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
   if (B == 0 || H == 0 || N == 0) {
     *empty = true;
@@ -493,43 +495,45 @@ int check_fp8(const void* q8, const void* k8, const void* v8t, const int32_t* qs
 }  // namespace
 
 extern "C" int flash_attn_quantize_fp8_validate(const void* x, void* x8, int32_t* scale_codes, int64_t B, int64_t H,
-                                                int64_t N, int64_t d, int layout, void* /*stream*/, int dtype) {
+                                                int64_t N, int64_t d, int layout, void* /*stream*/, int dtype,
+                                                int format) {
   fa::QuantArgs a;
   bool empty;
-  return check_quant(x, x8, scale_codes, B, H, N, d, layout, dtype, &a, &empty);
+  return check_quant(x, x8, scale_codes, B, H, N, d, layout, dtype, format, &a, &empty);
 }
 
 extern "C" int flash_attn_quantize_fp8(const void* x, void* x8, int32_t* scale_codes, int64_t B, int64_t H,
-                                       int64_t N, int64_t d, int layout, void* stream, int dtype) {
+                                       int64_t N, int64_t d, int layout, void* stream, int dtype, int format) {
   fa::QuantArgs a;
   bool empty;
-  const int st = check_quant(x, x8, scale_codes, B, H, N, d, layout, dtype, &a, &empty);
+  const int st = check_quant(x, x8, scale_codes, B, H, N, d, layout, dtype, format, &a, &empty);
   if (st != FA_OK || empty) return st;
   const hipError_t err = fa::launch_quant_fp8(a, dtype == FA_FP16, static_cast<int>(d), layout == FA_FP8_KEYS_T,
-                                              static_cast<hipStream_t>(stream));
+                                              format == FA_FP8_E5M2, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 extern "C" int flash_attn_fwd_fp8_validate(const void* q8, const void* k8, const void* v8t, const int32_t* q_scale,
                                            const int32_t* k_scale, const int32_t* v_scale, void* o, float* lse,
                                            int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
-                                           void* /*stream*/, int out_dtype) {
+                                           void* /*stream*/, int out_dtype, int format) {
   fa::Fp8Args a;
   bool empty;
-  return check_fp8(q8, k8, v8t, q_scale, k_scale, v_scale, o, lse, B, H, N, d, causal, scale, out_dtype, &a,
+  return check_fp8(q8, k8, v8t, q_scale, k_scale, v_scale, o, lse, B, H, N, d, causal, scale, out_dtype, format, &a,
                    &empty);
 }
 
 extern "C" int flash_attn_fwd_fp8(const void* q8, const void* k8, const void* v8t, const int32_t* q_scale,
                                   const int32_t* k_scale, const int32_t* v_scale, void* o, float* lse, int64_t B,
                                   int64_t H, int64_t N, int64_t d, int causal, float scale, void* stream,
-                                  int out_dtype) {
+                                  int out_dtype, int format) {
   fa::Fp8Args a;
   bool empty;
   const int st = check_fp8(q8, k8, v8t, q_scale, k_scale, v_scale, o, lse, B, H, N, d, causal, scale, out_dtype,
-                           &a, &empty);
+                           format, &a, &empty);
   if (st != FA_OK || empty) return st;
-  const hipError_t err = fa::launch_fwd_fp8(a, out_dtype == FA_FP16, causal == 1, static_cast<hipStream_t>(stream));
+  const hipError_t err = fa::launch_fwd_fp8(a, out_dtype == FA_FP16, causal == 1, format == FA_FP8_E5M2,
+                                            static_cast<hipStream_t>(stream));
   return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

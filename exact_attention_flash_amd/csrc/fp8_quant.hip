@@ -1,15 +1,16 @@
-// FP8 (E4M3) block quantization for the FP8 attention forward on gfx950.
+// FP8 (E4M3 or E5M2) block quantization for the FP8 attention forward on gfx950.
 //
 // "FlashAttention: IO-Aware Tiling, Online Softmax Mathematics, Memory Hierarchy
 // Dynamics, and Kernel Evolution", section on FlashAttention-3, runs attention in
 // 8-bit floating point with block-level quantization and dynamic scaling factors.
 // Here a block is 64 consecutive rows of one (batch, head) slice; its scale is the
 // power of two 2^e with e the smallest integer such that the block's largest
-// magnitude a satisfies a <= 448 * 2^e (448: the largest finite E4M3 value; e = 0
-// for an all-zero block; e limited to the E8M0 range [-127, 127]), and each value
-// is stored as E4M3(x / 2^e), rounded to nearest even by v_cvt_pk_fp8_f32. The
-// division by 2^e is exact in fp32. The scale is kept as its E8M0 code e + 127,
-// the form the scaled matrix instructions take.
+// magnitude a satisfies a <= F * 2^e (F the format's largest finite value: 448 for
+// E4M3, 57344 for E5M2; e = 0 for an all-zero block; e limited to the E8M0 range
+// [-127, 127]), and each value is stored as FP8(x / 2^e), rounded to nearest even by
+// v_cvt_pk_fp8_f32 (E4M3) or v_cvt_pk_bf8_f32 (E5M2). The division by 2^e is exact
+// in fp32. The scale is kept as its E8M0 code e + 127, the form the scaled matrix
+// instructions take.
 //
 // One workgroup of 256 lanes per block: 16-byte loads, a maximum reduction, then
 // either row-major E4M3 (queries, keys) or the keys-transposed layout of values,
@@ -45,21 +46,29 @@ __device__ __forceinline__ void unpack8(const u32x4 w, bool fp16, float (&f)[8])
   }
 }
 
-// four E4M3 codes (round to nearest even): a in byte 0 ... d in byte 3
+// four E4M3 (E5 false) or E5M2 (E5 true) codes, rounded to nearest even: a in byte
+// 0 ... d in byte 3
+template <bool E5>
 __device__ __forceinline__ uint32_t pack4(float a, float b, float c, float d) {
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false), true);
+  if constexpr (E5)
+    return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(c, d, __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false), true);
+  else
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false), true);
 }
 
-// smallest e with amax <= 448 * 2^e (exact: 448 = 0.875 * 2^9), in [-127, 127]
+// smallest e with amax <= F * 2^e, F the format's largest finite value (exact: 448 =
+// 0.875 * 2^9, 57344 = 0.875 * 2^16), in [-127, 127]
+template <bool E5>
 __device__ __forceinline__ int block_exp(float amax) {
   if (!(amax > 0.f)) return 0;
   int E;
   const float m = frexpf(amax, &E);  // amax = m * 2^E, m in [0.5, 1)
-  int e = (m > 0.875f) ? E - 8 : E - 9;
+  constexpr int kTop = E5 ? 16 : 9;
+  int e = (m > 0.875f) ? E - kTop + 1 : E - kTop;
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
-template <bool FP16, int D, bool VT>
+template <bool FP16, int D, bool VT, bool E5>
 __global__ __launch_bounds__(kThreads) void quant_fp8(QuantArgs a) {
   constexpr int kChunks = kFp8Block * D / 8;          // 16-byte input chunks per block
   constexpr int kPer = kChunks / kThreads;             // per lane
@@ -87,7 +96,7 @@ __global__ __launch_bounds__(kThreads) void quant_fp8(QuantArgs a) {
   if ((tid & 63) == 0) wmax[tid >> 6] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-  const int e = block_exp(amax);
+  const int e = block_exp<E5>(amax);
   const float inv = ldexpf(1.0f, -e);
   if (tid == 0) a.se[(int64_t)bh * a.t64 + t] = e + 127;
 
@@ -97,8 +106,8 @@ __global__ __launch_bounds__(kThreads) void quant_fp8(QuantArgs a) {
       const int c = tid + kThreads * i, r = c / kCpr, c8 = c % kCpr;
       if (row0 + r < a.n) {
         const float* f = v[i];
-        const u32x2 w = {pack4(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv),
-                         pack4(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv)};
+        const u32x2 w = {pack4<E5>(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv),
+                         pack4<E5>(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv)};
         *reinterpret_cast<u32x2*>(a.x8 + ((int64_t)bh * a.n + row0 + r) * D + c8 * 8) = w;
       }
     }
@@ -121,27 +130,34 @@ __global__ __launch_bounds__(kThreads) void quant_fp8(QuantArgs a) {
       u32x4 w;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        w[q] = pack4(tile[kb + 8 * q + 0][col], tile[kb + 8 * q + 1][col], tile[kb + 8 * q + 2][col],
-                     tile[kb + 8 * q + 3][col]);
+        w[q] = pack4<E5>(tile[kb + 8 * q + 0][col], tile[kb + 8 * q + 1][col], tile[kb + 8 * q + 2][col],
+                         tile[kb + 8 * q + 3][col]);
       *reinterpret_cast<u32x4*>(out + (int64_t)col * kFp8Block + 16 * g4) = w;
     }
   }
 }
 
-template <bool FP16, int D>
+template <bool FP16, int D, bool E5>
 hipError_t launch2(const QuantArgs& a, bool vt, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)a.bh * a.t64));
-  if (vt) hipLaunchKernelGGL((quant_fp8<FP16, D, true>), grid, dim3(kThreads), 0, stream, a);
-  else hipLaunchKernelGGL((quant_fp8<FP16, D, false>), grid, dim3(kThreads), 0, stream, a);
+  if (vt) hipLaunchKernelGGL((quant_fp8<FP16, D, true, E5>), grid, dim3(kThreads), 0, stream, a);
+  else hipLaunchKernelGGL((quant_fp8<FP16, D, false, E5>), grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
+}
+
+template <bool E5>
+hipError_t launch_fmt(const QuantArgs& a, bool fp16, int d, bool vt, hipStream_t stream) {
+  if (fp16) return d == 64 ? launch2<true, 64, E5>(a, vt, stream) : launch2<true, 128, E5>(a, vt, stream);
+  return d == 64 ? launch2<false, 64, E5>(a, vt, stream) : launch2<false, 128, E5>(a, vt, stream);
 }
 
 }  // namespace fp8q
 
-hipError_t launch_quant_fp8(const QuantArgs& a, bool fp16, int d, bool keys_transposed, hipStream_t stream) {
+hipError_t launch_quant_fp8(const QuantArgs& a, bool fp16, int d, bool keys_transposed, bool e5m2,
+                            hipStream_t stream) {
   using namespace fp8q;
-  if (fp16) return d == 64 ? launch2<true, 64>(a, keys_transposed, stream) : launch2<true, 128>(a, keys_transposed, stream);
-  return d == 64 ? launch2<false, 64>(a, keys_transposed, stream) : launch2<false, 128>(a, keys_transposed, stream);
+  return e5m2 ? launch_fmt<true>(a, fp16, d, keys_transposed, stream)
+              : launch_fmt<false>(a, fp16, d, keys_transposed, stream);
 }
 
 }  // namespace fa

@@ -1,4 +1,4 @@
-// Exact attention forward on FP8 (E4M3) inputs for gfx950, d = 128, bf16/fp16 out.
+// Exact attention forward on FP8 (E4M3 or E5M2) inputs for gfx950, d = 128, bf16/fp16 out.
 //
 // "FlashAttention: IO-Aware Tiling, Online Softmax Mathematics, Memory Hierarchy
 // Dynamics, and Kernel Evolution", section on FlashAttention-3: attention in 8-bit
@@ -10,8 +10,9 @@
 // movement before counting FLOPs", section 02): running maximum m, denominator l,
 // unnormalised u, O = u / l and LSE = m + ln l at the end.
 //
-// Both products run on v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x E4M3, fp32
-// accumulate) with the blocks' E8M0 scales as the instruction's operand scales,
+// Both products run on v_mfma_scale_f32_32x32x64_f8f6f4 (the inputs' format for Q, K
+// and V, E4M3 for P; fp32 accumulate) with the blocks' E8M0 scales as the
+// instruction's operand scales,
 // so every score and every P V contribution is exact in scale:
 //  * S^T = K Q^T: A = 32 key rows of the K tile (LDS), B = the wave's 32 query
 //    rows (registers), two k-steps of 64 over d; scales = the K tile's and the Q
@@ -66,17 +67,21 @@ constexpr int kQLoads = kQBytes / 1024 / kWaves + 1;            // Q blocks + th
 __device__ __forceinline__ int swz8(int row) { return (((row >> 1) & 1) << 2) | ((row >> 2) & 3); }
 __device__ __forceinline__ int swz4(int row) { return (row >> 2) & 3; }
 
+// FA (A operand) and FB (B operand) select the instruction's operand formats: 0 =
+// E4M3, 1 = E5M2
+template <int FA, int FB>
 __device__ __forceinline__ f32x16 mfma8(const u32x4 a0, const u32x4 a1, const i32x8 b, f32x16 c, int sa, int sb) {
   const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, sa, 0, sb);
 }
 
 __device__ __forceinline__ int pack4(float a, float b, float c, float d) {
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false), true);
 }
 
-template <bool FP16OUT, bool CAUSAL>
+template <bool FP16OUT, bool CAUSAL, bool E5>
 __global__ __launch_bounds__(kThreads, 1) void fwd_fp8(Fp8Args a) {
+  constexpr int kIn = E5 ? 1 : 0;  // format code of Q, K and V; P is always E4M3
   __shared__ __attribute__((aligned(1024))) char smem[kStages * kStage + kQBytes + kScale];
   char* const qsm = smem + kStages * kStage;
   char* const qscale = qsm + kQBytes;
@@ -240,8 +245,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8(Fp8Args a) {
     for (int st = 0; st < 4; ++st) {
       if (st + 1 < 4) issue(st + 1);
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (DO_S) s[st & 1] = mfma8(ka[st & 1][0], ka[st & 1][1], qreg[st >> 1], s[st & 1], ks, q_sc);
-      if constexpr (DO_P) acc[st] = mfma8(va[st & 1][0], va[st & 1][1], pb, acc[st], vs, one);
+      if constexpr (DO_S) s[st & 1] = mfma8<kIn, kIn>(ka[st & 1][0], ka[st & 1][1], qreg[st >> 1], s[st & 1], ks, q_sc);
+      if constexpr (DO_P) acc[st] = mfma8<kIn, 0>(va[st & 1][0], va[st & 1][1], pb, acc[st], vs, one);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -359,7 +364,20 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8(Fp8Args a) {
 
 }  // namespace f8
 
-hipError_t launch_fwd_fp8(const Fp8Args& args, bool fp16_out, bool causal, hipStream_t stream) {
+template <bool E5>
+hipError_t launch_fmt(const Fp8Args& a, int grid, bool fp16_out, bool causal, hipStream_t stream) {
+  using namespace f8;
+  if (fp16_out) {
+    if (causal) hipLaunchKernelGGL((fwd_fp8<true, true, E5>), dim3(grid), dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL((fwd_fp8<true, false, E5>), dim3(grid), dim3(kThreads), 0, stream, a);
+  } else {
+    if (causal) hipLaunchKernelGGL((fwd_fp8<false, true, E5>), dim3(grid), dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL((fwd_fp8<false, false, E5>), dim3(grid), dim3(kThreads), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_fp8(const Fp8Args& args, bool fp16_out, bool causal, bool e5m2, hipStream_t stream) {
   using namespace f8;
   Fp8Args a = args;
   const int cus = device_cus();
@@ -370,14 +388,7 @@ hipError_t launch_fwd_fp8(const Fp8Args& args, bool fp16_out, bool causal, hipSt
     grid &= ~7;
     if (grid < 8) grid = 8;
   }
-  if (fp16_out) {
-    if (causal) hipLaunchKernelGGL((fwd_fp8<true, true>), dim3(grid), dim3(kThreads), 0, stream, a);
-    else hipLaunchKernelGGL((fwd_fp8<true, false>), dim3(grid), dim3(kThreads), 0, stream, a);
-  } else {
-    if (causal) hipLaunchKernelGGL((fwd_fp8<false, true>), dim3(grid), dim3(kThreads), 0, stream, a);
-    else hipLaunchKernelGGL((fwd_fp8<false, false>), dim3(grid), dim3(kThreads), 0, stream, a);
-  }
-  return hipGetLastError();
+  return e5m2 ? launch_fmt<true>(a, grid, fp16_out, causal, stream) : launch_fmt<false>(a, grid, fp16_out, causal, stream);
 }
 
 }  // namespace fa

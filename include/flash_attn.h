@@ -35,6 +35,10 @@ typedef enum { FA_BF16 = 0, FA_FP16 = 1 } fa_dtype;
 /* Layouts written by flash_attn_quantize_fp8. */
 typedef enum { FA_FP8_ROWS = 0, FA_FP8_KEYS_T = 1 } fa_fp8_layout;
 
+/* FP8 formats (OCP 8-bit floating point) of flash_attn_quantize_fp8 and
+ * flash_attn_fwd_fp8. */
+typedef enum { FA_FP8_E4M3 = 0, FA_FP8_E5M2 = 1 } fa_fp8_format;
+
 /* Return codes. Every check runs on the host before anything is launched. */
 typedef enum {
   FA_OK = 0,
@@ -46,7 +50,8 @@ typedef enum {
   FA_ERR_ALIGN = -6,   /* a 16-bit tensor not 16-byte aligned, or an fp32 one not 4-byte aligned */
   FA_ERR_ALIAS = -7,   /* an output overlaps an input or another output          */
   FA_ERR_HIP = -8,     /* the HIP runtime reported an error at launch             */
-  FA_ERR_ARG = -9,     /* causal is not 0 or 1, or num_splits is negative        */
+  FA_ERR_ARG = -9,     /* causal is not 0 or 1, num_splits is negative, or an FP8
+                          layout or format is not one of the defined values       */
   FA_ERR_WORKSPACE = -10, /* split workspace NULL, not 16-byte aligned or too small */
   FA_ERR_STRIDE = -11, /* strided call: a stride negative, not a multiple of 8 elements, a row
                           stride below d or >= 2^23, a slice spanning >= 2 GiB, or o / lse
@@ -160,18 +165,19 @@ int flash_attn_fwd_strided_validate(const void* q, const void* k, const void* v,
 
 /*
  * flash_attn_quantize_fp8 -- block quantization of a contiguous [B, H, N, d] bf16 /
- * fp16 tensor to FP8 E4M3 for flash_attn_fwd_fp8 ("FlashAttention: IO-Aware
- * Tiling, Online Softmax Mathematics, Memory Hierarchy Dynamics, and Kernel
- * Evolution", section on FlashAttention-3: FP8 with block-level quantization and
- * dynamic scaling factors).
+ * fp16 tensor to FP8 (E4M3 or E5M2) for flash_attn_fwd_fp8 ("FlashAttention:
+ * IO-Aware Tiling, Online Softmax Mathematics, Memory Hierarchy Dynamics, and Kernel
+ * Evolution", section on FlashAttention-3: FP8 E4M3/E5M2 with block-level
+ * quantization and dynamic scaling factors).
  *
  * A block is 64 consecutive rows (keys) of one (batch, head) slice; T = ceil(N/64)
  * blocks per slice. Block t's scale is 2^e with e the smallest integer such that
- * its largest magnitude a satisfies a <= 448 * 2^e (e = 0 for an all-zero block;
- * e limited to [-127, 127]); each value is stored as the OCP E4M3 code of x / 2^e
- * (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, largest finite 448),
- * rounded to nearest even. The value a code c of block t stands for is
- * decode(c) * 2^e.
+ * its largest magnitude a satisfies a <= F * 2^e, F the format's largest finite
+ * value (e = 0 for an all-zero block; e limited to [-127, 127]); each value is
+ * stored as the OCP code of x / 2^e, rounded to nearest even:
+ *   FA_FP8_E4M3: 1 sign, 4 exponent bits with bias 7, 3 mantissa bits, F = 448;
+ *   FA_FP8_E5M2: 1 sign, 5 exponent bits with bias 15, 2 mantissa bits, F = 57344.
+ * The value a code c of block t stands for is decode(c) * 2^e.
  *
  * x           : device, contiguous [B, H, N, d] of `dtype` (FA_BF16 / FA_FP16). Read only.
  * x8          : device, written. layout FA_FP8_ROWS: [B, H, N, d] bytes (row-major,
@@ -182,16 +188,17 @@ int flash_attn_fwd_strided_validate(const void* q, const void* k, const void* v,
  *               keys at or past N are 0.
  * scale_codes : device, written, [B, H, T] int32: e + 127 (the E8M0 code of 2^e).
  * d           : 64 or 128.  layout: FA_FP8_ROWS or FA_FP8_KEYS_T (else FA_ERR_ARG).
+ * format      : FA_FP8_E4M3 or FA_FP8_E5M2 (else FA_ERR_ARG).
  * stream, ownership, errors: as for flash_attn_fwd. Alignment: x and x8 16 bytes,
  * scale_codes 4 (FA_ERR_ALIGN); x8 and scale_codes must not overlap x or each
  * other (FA_ERR_ALIAS). Requires N * d < 2^31 and B * H * T < 2^31.
  */
 int flash_attn_quantize_fp8(const void* x, void* x8, int32_t* scale_codes, int64_t B, int64_t H, int64_t N,
-                            int64_t d, int layout, void* stream, int dtype);
+                            int64_t d, int layout, void* stream, int dtype, int format);
 
 /* flash_attn_quantize_fp8_validate -- its checks alone; no HIP call. */
 int flash_attn_quantize_fp8_validate(const void* x, void* x8, int32_t* scale_codes, int64_t B, int64_t H,
-                                     int64_t N, int64_t d, int layout, void* stream, int dtype);
+                                     int64_t N, int64_t d, int layout, void* stream, int dtype, int format);
 
 /*
  * flash_attn_fwd_fp8 -- the attention forward on FP8 inputs: o and lse are the
@@ -201,13 +208,15 @@ int flash_attn_quantize_fp8_validate(const void* x, void* x8, int32_t* scale_cod
  * rounded to E4M3 for the P V product (relative to the row maximum, times 2^8),
  * while the row sums use them unrounded.
  *
- * q8, k8  : device, [B, H, N, 128] E4M3 from flash_attn_quantize_fp8 (FA_FP8_ROWS).
- * v8t     : device, [B, H, T, 128, 64] E4M3 from flash_attn_quantize_fp8 (FA_FP8_KEYS_T).
+ * q8, k8  : device, [B, H, N, 128] FP8 codes from flash_attn_quantize_fp8 (FA_FP8_ROWS).
+ * v8t     : device, [B, H, T, 128, 64] FP8 codes from flash_attn_quantize_fp8 (FA_FP8_KEYS_T).
  * q_scale, k_scale, v_scale : device, [B, H, T] int32 scale codes of q8, k8, v8t.
  * o       : device, written, contiguous [B, H, N, 128] of out_dtype.
  * lse     : device, written, contiguous [B, H, N] fp32.
  * d       : 128 (FA_ERR_HEADDIM otherwise). causal, scale, stream: as for flash_attn_fwd.
  * out_dtype : FA_BF16 or FA_FP16.
+ * format  : FA_FP8_E4M3 or FA_FP8_E5M2, the format of q8, k8 and v8t (all three;
+ *           else FA_ERR_ARG). P is rounded to E4M3 in either case.
  * Ownership and errors as for flash_attn_fwd; 16-byte alignment for q8, k8, v8t, o
  * and 4 for the scale arrays and lse; o and lse must not overlap an input or each
  * other.
@@ -215,13 +224,13 @@ int flash_attn_quantize_fp8_validate(const void* x, void* x8, int32_t* scale_cod
 int flash_attn_fwd_fp8(const void* q8, const void* k8, const void* v8t, const int32_t* q_scale,
                        const int32_t* k_scale, const int32_t* v_scale, void* o, float* lse,
                        int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
-                       void* stream, int out_dtype);
+                       void* stream, int out_dtype, int format);
 
 /* flash_attn_fwd_fp8_validate -- its checks alone; no HIP call. */
 int flash_attn_fwd_fp8_validate(const void* q8, const void* k8, const void* v8t, const int32_t* q_scale,
                                 const int32_t* k_scale, const int32_t* v_scale, void* o, float* lse,
                                 int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
-                                void* stream, int out_dtype);
+                                void* stream, int out_dtype, int format);
 
 /*
  * flash_attn_fwd_splitkv -- the forward pass with every query tile's keys cut
@@ -370,9 +379,9 @@ int flash_attn_bwd_validate(const void* q, const void* k, const void* v, const v
 /* Static, never-freed description of a status code (unknown codes included). */
 const char* flash_attn_strerror(int status);
 
-/* ABI version of this header, currently 6 (1: forward only; 2: + backward;
+/* ABI version of this header, currently 7 (1: forward only; 2: + backward;
  * 3: + key-split forward; 4: + strided forward; 5: + FP8 quantization and forward;
- * 6: + key-split forward without a caller workspace). */
+ * 6: + key-split forward without a caller workspace; 7: FP8 format argument, E5M2). */
 int flash_attn_abi_version(void);
 
 #ifdef __cplusplus

@@ -50,7 +50,7 @@ def test_library_loads_and_exports_header_symbols():
 
 
 def test_abi_version_and_strerror():
-    assert fa.flash_attn_abi_version() == 6
+    assert fa.flash_attn_abi_version() == 7
     codes = [fa.FA_OK, fa.FA_ERR_NULL, fa.FA_ERR_SHAPE, fa.FA_ERR_HEADDIM, fa.FA_ERR_DTYPE,
              fa.FA_ERR_SCALE, fa.FA_ERR_ALIGN, fa.FA_ERR_ALIAS, fa.FA_ERR_HIP, fa.FA_ERR_ARG,
              fa.FA_ERR_WORKSPACE, fa.FA_ERR_STRIDE, fa.FA_ERR_SCRATCH]
@@ -405,12 +405,13 @@ def test_strided_empty_problem_is_a_noop(kw):
 
 # ---- FP8 ----
 
-def _qargs(x=A, x8=A + GB, se=A + 2 * GB, B=1, H=2, N=100, d=128, layout=0, stream=None, dtype=0):
-    return (x, x8, se, B, H, N, d, layout, stream, dtype)
+def _qargs(x=A, x8=A + GB, se=A + 2 * GB, B=1, H=2, N=100, d=128, layout=0, stream=None, dtype=0, fmt=0):
+    return (x, x8, se, B, H, N, d, layout, stream, dtype, fmt)
 
 
 BAD_QUANT = [
     (dict(d=96), fa.FA_ERR_HEADDIM), (dict(layout=2), fa.FA_ERR_ARG), (dict(dtype=5), fa.FA_ERR_DTYPE),
+    (dict(fmt=2), fa.FA_ERR_ARG), (dict(fmt=-1), fa.FA_ERR_ARG),
     (dict(N=-1), fa.FA_ERR_SHAPE), (dict(x=None), fa.FA_ERR_NULL), (dict(se=None), fa.FA_ERR_NULL),
     (dict(x8=A + GB + 8), fa.FA_ERR_ALIGN), (dict(se=A + 2 * GB + 2), fa.FA_ERR_ALIGN),
     (dict(x8=A + 16), fa.FA_ERR_ALIAS), (dict(se=A + GB + 64), fa.FA_ERR_ALIAS),
@@ -425,7 +426,8 @@ def test_quantize_rejects(kw, code):
     assert _native.quantize_raw(*_qargs(**kw)) == code
 
 
-@pytest.mark.parametrize("kw", [dict(), dict(layout=1), dict(d=64, dtype=1), dict(se=A + GB + 2 * 100 * 128)])
+@pytest.mark.parametrize("kw", [dict(), dict(layout=1), dict(d=64, dtype=1), dict(se=A + GB + 2 * 100 * 128),
+                                dict(fmt=fa.FA_FP8_E5M2), dict(fmt=fa.FA_FP8_E5M2, layout=1)])
 def test_quantize_accepts(kw):
     assert _native.validate_quantize_raw(*_qargs(**kw)) == fa.FA_OK
 
@@ -435,12 +437,14 @@ def test_quantize_empty_is_a_noop():
 
 
 def _fargs(q8=A, k8=A + GB, v8t=A + 2 * GB, qs=A + 3 * GB, ks=A + 3 * GB + 4096, vs=A + 3 * GB + 8192,
-           o=A + 4 * GB, lse=A + 5 * GB, B=1, H=2, N=100, d=128, causal=0, scale=0.1, stream=None, dtype=0):
-    return (q8, k8, v8t, qs, ks, vs, o, lse, B, H, N, d, causal, scale, stream, dtype)
+           o=A + 4 * GB, lse=A + 5 * GB, B=1, H=2, N=100, d=128, causal=0, scale=0.1, stream=None, dtype=0,
+           fmt=0):
+    return (q8, k8, v8t, qs, ks, vs, o, lse, B, H, N, d, causal, scale, stream, dtype, fmt)
 
 
 BAD_FP8 = [
     (dict(d=64), fa.FA_ERR_HEADDIM), (dict(dtype=2), fa.FA_ERR_DTYPE), (dict(causal=3), fa.FA_ERR_ARG),
+    (dict(fmt=7), fa.FA_ERR_ARG),
     (dict(scale=0.0), fa.FA_ERR_SCALE), (dict(B=-1), fa.FA_ERR_SHAPE),
     (dict(v8t=None), fa.FA_ERR_NULL), (dict(ks=None), fa.FA_ERR_NULL), (dict(lse=None), fa.FA_ERR_NULL),
     (dict(q8=A + 4), fa.FA_ERR_ALIGN), (dict(vs=A + 3 * GB + 8194), fa.FA_ERR_ALIGN),
@@ -458,5 +462,6 @@ def test_fp8_rejects(kw, code):
 def test_fp8_accepts_and_empty():
     assert _native.validate_fp8_raw(*_fargs()) == fa.FA_OK
     assert _native.validate_fp8_raw(*_fargs(causal=1, dtype=1)) == fa.FA_OK
+    assert _native.validate_fp8_raw(*_fargs(fmt=fa.FA_FP8_E5M2)) == fa.FA_OK
     assert _native.fp8_raw(*_fargs(q8=None, k8=None, v8t=None, qs=None, ks=None, vs=None, o=None, lse=None,
                                    H=0)) == fa.FA_OK
