@@ -37,6 +37,7 @@
 
 #include "bwd_kernel.h"
 #include "gfx950_ops.h"
+#include "launch_log.h"
 
 namespace fa {
 namespace bwd {
@@ -593,10 +594,14 @@ hipError_t launch_all(const BwdArgs& a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int q_tiles = (a.n + kDqRows - 1) / kDqRows;
+  const int k_blocks = (a.n + kKvRows - 1) / kKvRows;
+  launch_log("bwd_delta<%s, %d> grid %lld x 256; bwd_dq<%s, %d, %s> grid %d x %d; bwd_dkdv<%s, %d, %s> grid %d x %d",
+             dtype_name(FP16), D, (long long)((rows + kRowsPerBlock - 1) / kRowsPerBlock), dtype_name(FP16), D,
+             CAUSAL ? "causal" : "full", a.bh * q_tiles, 64 * kDqWaves, dtype_name(FP16), D,
+             CAUSAL ? "causal" : "full", a.bh * k_blocks, 64 * kKvWaves);
   hipLaunchKernelGGL((bwd_dq<FP16, D, CAUSAL>), dim3(a.bh * q_tiles), dim3(64 * kDqWaves), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int k_blocks = (a.n + kKvRows - 1) / kKvRows;
   hipLaunchKernelGGL((bwd_dkdv<FP16, D, CAUSAL>), dim3(a.bh * k_blocks), dim3(64 * kKvWaves), 0, stream, a);
   return hipGetLastError();
 }

@@ -83,7 +83,7 @@ int check_args(const void* q, const void* k, const void* v, void* o, float* lse,
   // indexing limits: a (batch, head) slice is addressed with 32-bit offsets,
   // workgroups with a 32-bit grid
   const int64_t rows = fa::rows_per_workgroup();
-  if (N * d > INT32_MAX - 1) return FA_ERR_SHAPE;
+  if (N > (INT32_MAX - 1) / d) return FA_ERR_SHAPE;
   if (B > INT32_MAX / H) return FA_ERR_SHAPE;
   const int64_t bh = B * H;
   const int64_t q_tiles = (N + rows - 1) / rows;
@@ -351,7 +351,8 @@ extern "C" int flash_attn_fwd_splitkv_plan(int64_t B, int64_t H, int64_t N, int6
   if (d != 64 && d != 128) return FA_ERR_HEADDIM;
   if (causal != 0 && causal != 1) return FA_ERR_ARG;
   if (B == 0 || H == 0 || N == 0) return 1;
-  if (B > INT32_MAX / H) return FA_ERR_SHAPE;
+  // the forward's indexing limits (also keep the item count below far from overflow)
+  if (N > (INT32_MAX - 1) / d || B > INT32_MAX / H) return FA_ERR_SHAPE;
   return plan_splits(B * H, N, causal, cus);
 }
 
@@ -361,8 +362,12 @@ extern "C" int64_t flash_attn_fwd_splitkv_workspace_size(int64_t B, int64_t H, i
   if (d != 64 && d != 128) return FA_ERR_HEADDIM;
   if ((causal != 0 && causal != 1) || num_splits < 1) return FA_ERR_ARG;
   if (B == 0 || H == 0 || N == 0) return 0;
-  if (B > INT32_MAX / H) return FA_ERR_SHAPE;
-  return static_cast<int64_t>(workspace_bytes_for(B * H, N, d, resolve_splits(N, causal, num_splits)));
+  // the split forward's indexing limits: then the byte count stays far inside 64 bits
+  if (N > (INT32_MAX - 1) / d || B > INT32_MAX / H) return FA_ERR_SHAPE;
+  const int splits = resolve_splits(N, causal, num_splits);
+  const int64_t items = B * H * ((N + fa::rows_per_workgroup() - 1) / fa::rows_per_workgroup());
+  if (items > INT32_MAX / splits) return FA_ERR_SHAPE;
+  return static_cast<int64_t>(workspace_bytes_for(B * H, N, d, splits));
 }
 
 namespace {
@@ -426,7 +431,7 @@ int check_quant(const void* x, void* x8, int32_t* se, int64_t B, int64_t H, int6
     *empty = true;
     return FA_OK;
   }
-  if (N * d > INT32_MAX - 1 || B > INT32_MAX / H) return FA_ERR_SHAPE;
+  if (N > (INT32_MAX - 1) / d || B > INT32_MAX / H) return FA_ERR_SHAPE;
   const int64_t bh = B * H, t64 = (N + fa::kFp8Block - 1) / fa::kFp8Block;
   if (bh > INT32_MAX / t64) return FA_ERR_SHAPE;
   if (!x || !x8 || !se) return FA_ERR_NULL;
@@ -459,7 +464,7 @@ int check_fp8(const void* q8, const void* k8, const void* v8t, const int32_t* qs
     *empty = true;
     return FA_OK;
   }
-  if (N * d > INT32_MAX - 1 || B > INT32_MAX / H) return FA_ERR_SHAPE;
+  if (N > (INT32_MAX - 1) / d || B > INT32_MAX / H) return FA_ERR_SHAPE;
   const int64_t bh = B * H, t64 = (N + fa::kFp8Block - 1) / fa::kFp8Block;
   const int64_t q_tiles = (N + fa::rows_per_workgroup() - 1) / fa::rows_per_workgroup();
   if (bh > INT32_MAX / t64) return FA_ERR_SHAPE;
@@ -554,7 +559,7 @@ int check_bwd_args(const void* q, const void* k, const void* v, const void* o, c
     return FA_OK;
   }
   // a slice is addressed with 32-bit offsets; grids of bh * ceil(N / 128) workgroups
-  if (N * d > INT32_MAX - 1) return FA_ERR_SHAPE;
+  if (N > (INT32_MAX - 1) / d) return FA_ERR_SHAPE;
   if (B > INT32_MAX / H) return FA_ERR_SHAPE;
   const int64_t bh = B * H;
   if (bh > INT32_MAX / ((N + 127) / 128)) return FA_ERR_SHAPE;

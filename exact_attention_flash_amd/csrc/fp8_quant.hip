@@ -23,6 +23,7 @@
 
 #include "fp8_kernel.h"
 #include "gfx950_ops.h"
+#include "launch_log.h"
 
 namespace fa {
 namespace fp8q {
@@ -156,6 +157,8 @@ hipError_t launch_fmt(const QuantArgs& a, bool fp16, int d, bool vt, hipStream_t
 hipError_t launch_quant_fp8(const QuantArgs& a, bool fp16, int d, bool keys_transposed, bool e5m2,
                             hipStream_t stream) {
   using namespace fp8q;
+  launch_log("quant_fp8<%s, %d, %s, %s> grid %lld x %d", dtype_name(fp16), d, keys_transposed ? "keys-transposed" : "rows",
+             e5m2 ? "E5M2" : "E4M3", (long long)a.bh * a.t64, kThreads);
   return e5m2 ? launch_fmt<true>(a, fp16, d, keys_transposed, stream)
               : launch_fmt<false>(a, fp16, d, keys_transposed, stream);
 }

@@ -38,6 +38,7 @@
 #include "fp8_kernel.h"
 #include "fwd_kernel.h"
 #include "gfx950_ops.h"
+#include "launch_log.h"
 
 namespace fa {
 namespace f8 {
@@ -388,6 +389,8 @@ hipError_t launch_fwd_fp8(const Fp8Args& args, bool fp16_out, bool causal, bool 
     grid &= ~7;
     if (grid < 8) grid = 8;
   }
+  launch_log("fwd_fp8<%s out, %s, %s> grid %d x %d", dtype_name(fp16_out), causal ? "causal" : "full",
+             e5m2 ? "E5M2" : "E4M3", grid, kThreads);
   return e5m2 ? launch_fmt<true>(a, grid, fp16_out, causal, stream) : launch_fmt<false>(a, grid, fp16_out, causal, stream);
 }
 

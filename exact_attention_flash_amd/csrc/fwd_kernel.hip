@@ -77,6 +77,7 @@
 
 #include "fwd_kernel.h"
 #include "gfx950_ops.h"
+#include "launch_log.h"
 
 namespace fa {
 namespace pp {
@@ -614,12 +615,15 @@ __global__ __launch_bounds__(256) void merge_splits(FwdArgs a) {
 
 template <bool FP16, int D, bool CAUSAL>
 hipError_t launch_one(const FwdArgs& a, hipStream_t stream) {
+  launch_log("fwd_pingpong<%s, %d, %s, %s> grid %d x %d, %d splits", dtype_name(FP16), D, CAUSAL ? "causal" : "full",
+             a.splits > 1 ? "split" : "whole", a.grid, kThreads, a.splits);
   if (a.splits > 1) {
     hipLaunchKernelGGL((fwd_pingpong<FP16, D, CAUSAL, true>), dim3(a.grid), dim3(kThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     constexpr int kRows = 256 / (D / 4);
     const int64_t rows = (int64_t)a.bh * a.n;
+    launch_log("merge_splits<%s, %d> grid %lld x 256", dtype_name(FP16), D, (long long)((rows + kRows - 1) / kRows));
     hipLaunchKernelGGL((merge_splits<FP16, D>), dim3((unsigned)((rows + kRows - 1) / kRows)), dim3(256), 0, stream,
                        a);
     return hipGetLastError();

@@ -47,6 +47,7 @@
 
 #include "fwd_kernel.h"
 #include "gfx950_ops.h"
+#include "launch_log.h"
 
 namespace fa {
 namespace sp {
@@ -1017,6 +1018,9 @@ hipError_t launch_fwd_sp(const FwdArgs& args, bool fp16, int d, bool causal, hip
   a.grp_shift = grp.shift;
   a.heads_mul = heads.mul;
   a.heads_shift = heads.shift;
+  launch_log("fwd_sp<%s, %d, %s> grid %d x %d, %lld items, %d workgroups per schedule group, %s order, d_real %d",
+             dtype_name(fp16), d, causal ? "causal" : "full", grid, kThreads, (long long)items, group_wgs,
+             a.slice_major ? "slice-major" : "rank-major", a.d_real);
   auto pick = [&](auto fp16c) -> hipError_t {
     constexpr bool F = decltype(fp16c)::value;
     switch (d) {

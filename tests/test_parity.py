@@ -302,6 +302,26 @@ def test_large_values_bf16_scale_exactly(fa, causal, split):
         assert np.array_equal(lb, lse)
 
 
+def test_launch_log_names_the_instance():
+    """FLASH_ATTN_LOG=1 (read once per process, hence a child process): every launch
+    prints its kernel instance and grid to stderr."""
+    import os
+    import subprocess
+
+    code = (
+        "import torch, exact_attention_flash_amd as fa\n"
+        "q = torch.randn(1, 8, 300, 128, device='cuda', dtype=torch.bfloat16)\n"
+        "o, lse = fa.forward(q, q, q, causal=True)\n"
+        "fa.backward(q, q, q, o, lse, torch.randn_like(q), causal=True)\n"
+        "torch.cuda.synchronize()\n")
+    env = dict(os.environ, FLASH_ATTN_LOG="1")
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, timeout=120)
+    assert res.returncode == 0, res.stderr[-2000:]
+    _log(res.stderr.strip())
+    assert "flash_attn: fwd_sp<bf16, 128, causal> grid 16 x 512, 16 items" in res.stderr
+    assert "bwd_dkdv<bf16, 128, causal>" in res.stderr
+
+
 @pytest.mark.parametrize("pattern", ["rising", "first_spike"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("dtype", [inputs.BF16, inputs.FP16])
