@@ -48,35 +48,51 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA, vendor figure
 PEAK_HBM_GBS = 8000.0
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense FP8 MFMA, vendor figure
-# sources of the kernel flash_attn_fwd launches (the software-pipelined forward)
-KERNEL_SOURCES = ["exact_attention_flash_amd/csrc/fwd_sp.hip", "exact_attention_flash_amd/csrc/fwd_kernel.h",
-                  "exact_attention_flash_amd/csrc/gfx950_ops.h"]
-KERNEL_NAME = "fwd_sp (flash_attn_fwd)"
+# the two forward kernels flash_attn_fwd can launch (flash_attn_fwd_kernel names the
+# one a shape runs): kernel symbol and the sources it is built from
+FWD_KERNELS = {
+    "pipelined": ("fwd_sp", ["exact_attention_flash_amd/csrc/fwd_sp.hip", "exact_attention_flash_amd/csrc/fwd_kernel.h",
+                             "exact_attention_flash_amd/csrc/gfx950_ops.h"]),
+    "pingpong": ("fwd_pingpong", ["exact_attention_flash_amd/csrc/fwd_kernel.hip",
+                                  "exact_attention_flash_amd/csrc/fwd_kernel.h",
+                                  "exact_attention_flash_amd/csrc/gfx950_ops.h"]),
+}
 # (batch, head) slices the oracle runs per workload in --table (all rows of each)
 TABLE_SLICES = {"single_head_n256_d64": 1, "mha_b4_h16_n1024_d64": 64, "llama7b_b2_h32_n4096_d128_causal": 8,
                 "longctx_b1_h32_n16384_d128_causal": 1, "stress_b3_h8_n4099_d128_sigma8": 6}
 BWD_FLOP_FACTOR = 2.5       # backward: S, dP, dV, dQ, dK products versus the forward's S and PV
-TRAFFIC_FILE = "profiles/fwd_sp_hbm_traffic.txt"
+TRAFFIC_FILE = "profiles/fwd_hbm_traffic.txt"
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def fwd_kernel_of(w, causal: bool) -> str:
+    """"pipelined" or "pingpong": the forward kernel flash_attn_fwd runs for workload w."""
+    import exact_attention_flash_amd as fa
+
+    return fa.flash_attn_fwd_kernel(w.N, w.d, causal)
+
+
+def kernel_symbol(kernel: str) -> str:
+    return FWD_KERNELS[kernel][0]
+
+
+def kernel_source_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in FWD_KERNELS[kernel][1]:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, causal: bool):
-    """HBM bytes per launch recorded for this kernel source, or None if stale/absent."""
+def measured_traffic(workload: str, causal: bool, kernel: str):
+    """HBM bytes per launch recorded for this kernel and its source, or None if stale/absent."""
     path = os.path.join(ROOT, TRAFFIC_FILE)
     if not os.path.exists(path):
         return None
-    want = kernel_source_hash()
+    want = kernel_source_hash(kernel)
     with open(path) as f:
         for line in f:
             line = line.strip()
@@ -84,6 +100,7 @@ def measured_traffic(workload: str, causal: bool):
                 continue
             fields = dict(kv.split("=", 1) for kv in line.split())
             if (fields.get("workload") == workload and fields.get("causal") == str(int(causal))
+                    and fields.get("kernel") == kernel_symbol(kernel)
                     and fields.get("source_sha256_16") == want):
                 return float(fields["hbm_bytes_per_launch"])
     return None
@@ -453,7 +470,8 @@ def run(args, workload_name, causal):
     g, qkv = time_gpu(w, causal, args.steps, args.warmup)
     tflops = flops / (g["ms_per_step"] * 1e-3) / 1e12
     achieved = flops / (g["event_ms_per_launch"] * 1e-3) / 1e12
-    traffic = measured_traffic(workload_name, causal)
+    kernel = fwd_kernel_of(w, causal)
+    traffic = measured_traffic(workload_name, causal, kernel)
     line = {
         "metric": "attention fwd TFLOP/s and % of bf16 MFMA peak, N=4096 d=128 causal",
         "value": round(tflops, 2),
@@ -474,7 +492,7 @@ def run(args, workload_name, causal):
             "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": KERNEL_NAME,
+            "kernel": kernel_symbol(kernel),
             "flop_per_launch": flops,
             "launch_ms": round(g["event_ms_per_launch"], 5),
             "launch_ms_median": round(g["launch_ms_median"], 5),
@@ -484,7 +502,7 @@ def run(args, workload_name, causal):
         },
         "extra_alloc_bytes": g["extra_alloc_bytes"],
         "device": g["device"],
-        "kernel_source_sha256_16": kernel_source_hash(),
+        "kernel_source_sha256_16": kernel_source_hash(kernel),
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, causal, qkv, args.cpu_slices, g["gpu_out"])
@@ -502,16 +520,17 @@ def run_table(args):
             flops = w.flops(causal)
             med = g["launch_ms_median"]
             cb = cpu_baseline(w, causal, qkv, TABLE_SLICES[name], g["gpu_out"])
+            kernel = fwd_kernel_of(w, causal)
             print(json.dumps({
-                "workload": name, "dtype": w.dtype, "causal": causal, "kernel": KERNEL_NAME,
+                "workload": name, "dtype": w.dtype, "causal": causal, "kernel": kernel_symbol(kernel),
                 "launch_ms_median": round(med, 5), "launch_ms_p10": round(g["launch_ms_p10"], 5),
                 "launch_ms_p90": round(g["launch_ms_p90"], 5),
                 "tflops_at_median": round(flops / (med * 1e-3) / 1e12, 2),
                 "pct_of_bf16_peak": round(100.0 * flops / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
-                "hbm_bytes_per_launch": measured_traffic(name, causal),
+                "hbm_bytes_per_launch": measured_traffic(name, causal, kernel),
                 "compulsory_hbm_bytes": w.compulsory_bytes(),
                 "parity": cb["parity"], "oracle_seconds": round(cb["seconds"], 2), "oracle_cores": cb["cores"],
-                "kernel_source_sha256_16": kernel_source_hash(), "device": g["device"],
+                "kernel_source_sha256_16": kernel_source_hash(kernel), "device": g["device"],
                 "steps": args.steps, "warmup": args.warmup}), flush=True)
 
 

@@ -13,12 +13,13 @@ from . import _native
 from ._native import (FA_BF16, FA_FP16, FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEADDIM,  # noqa: F401
                       FA_ERR_DTYPE, FA_ERR_SCALE, FA_ERR_ALIGN, FA_ERR_ALIAS, FA_ERR_HIP, FA_ERR_ARG,
                       FA_ERR_WORKSPACE, FA_ERR_STRIDE, FA_ERR_SCRATCH, FA_SPLITKV_SCRATCH_BYTES,
-                      FA_FP8_ROWS, FA_FP8_KEYS_T, FA_FP8_E4M3, FA_FP8_E5M2)
+                      FA_FP8_ROWS, FA_FP8_KEYS_T, FA_FP8_E4M3, FA_FP8_E5M2, FA_FWD_KERNEL_PIPELINED,
+                      FA_FWD_KERNEL_PINGPONG)
 
 __all__ = ["forward", "backward", "forward_splitkv", "flash_attn_fwd", "flash_attn_fwd_strided",
            "flash_attn_fwd_splitkv", "flash_attn_fwd_splitkv_noalloc", "flash_attn_bwd",
            "splitkv_plan", "splitkv_workspace_size", "quantize_fp8", "flash_attn_fwd_fp8", "forward_fp8",
-           "flash_attn_strerror", "flash_attn_abi_version"]
+           "flash_attn_strerror", "flash_attn_abi_version", "flash_attn_fwd_kernel"]
 
 
 class FlashAttnError(RuntimeError):
@@ -361,3 +362,12 @@ def flash_attn_strerror(status: int) -> str:
 
 def flash_attn_abi_version() -> int:
     return _native.abi_version()
+
+
+def flash_attn_fwd_kernel(N: int, d: int, causal: bool = False) -> str:
+    """Name of the forward kernel an unsplit call of this shape runs: "pipelined" or
+    "pingpong" (flash_attn_fwd_kernel; FLASH_ATTN_FWD_KERNEL forces one)."""
+    st = _native.fwd_kernel(N, d, causal)
+    if st < 0:
+        raise FlashAttnError(st, "flash_attn_fwd_kernel")
+    return "pipelined" if st == FA_FWD_KERNEL_PIPELINED else "pingpong"

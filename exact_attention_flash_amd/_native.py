@@ -30,6 +30,8 @@ FA_FP8_ROWS = 0
 FA_FP8_KEYS_T = 1
 FA_FP8_E4M3 = 0
 FA_FP8_E5M2 = 1
+FA_FWD_KERNEL_PIPELINED = 1
+FA_FWD_KERNEL_PINGPONG = 2
 
 _lib = None
 
@@ -101,6 +103,8 @@ def lib() -> ctypes.CDLL:
         L.flash_attn_strerror.argtypes = [ctypes.c_int]
         L.flash_attn_abi_version.restype = ctypes.c_int
         L.flash_attn_abi_version.argtypes = []
+        L.flash_attn_fwd_kernel.restype = ctypes.c_int
+        L.flash_attn_fwd_kernel.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int]
         _lib = L
     return _lib
 
@@ -201,3 +205,8 @@ def strerror(status: int) -> str:
 
 def abi_version() -> int:
     return lib().flash_attn_abi_version()
+
+
+def fwd_kernel(N, d, causal) -> int:
+    """flash_attn_fwd_kernel: FA_FWD_KERNEL_PIPELINED or FA_FWD_KERNEL_PINGPONG, or a negative status."""
+    return lib().flash_attn_fwd_kernel(int(N), int(d), int(causal))

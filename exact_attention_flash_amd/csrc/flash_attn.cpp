@@ -24,24 +24,41 @@ bool overlaps(const void* a, uint64_t an, const void* b, uint64_t bn) {
 
 bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
-// Forward kernel of a call without a key split: the software-pipelined kernel, or
-// the ping-pong kernel when FLASH_ATTN_FWD_KERNEL=pingpong (read once per process;
-// kept for comparisons). Calls with a key split always use the ping-pong kernel's
-// split instance.
-// d is the smallest instance width (64, 80, 96 or 128) that holds the real head
-// dimension; the ping-pong kernel has the 64- and 128-wide instances only.
-hipError_t launch_unsplit(const fa::FwdArgs& a, bool fp16, int d, bool causal, hipStream_t stream) {
-  static const bool pingpong = [] {
-    const char* e = std::getenv("FLASH_ATTN_FWD_KERNEL");
-    return e != nullptr && std::strcmp(e, "pingpong") == 0;
-  }();
-  return pingpong ? fa::launch_fwd(a, fp16, d <= 64 ? 64 : 128, causal, stream)
-                  : fa::launch_fwd_sp(a, fp16, d, causal, stream);
+// Forward kernel of a call without a key split. The software-pipelined kernel
+// (fwd_sp.hip) overlaps each wave's softmax with its own products but pays more per
+// work item to fill and drain its pipeline; the ping-pong kernel (fwd_kernel.hip)
+// overlaps the two waves of a SIMD and starts items cheaply. Measured on one MI355X
+// over 20 shapes, the pipelined kernel is ahead (0.6-2.4%) once a work item's mean
+// key range reaches 4096 keys (non-causal N >= 4096, causal N >= 8K), and level or
+// behind (up to 15%) below that, the causal N = 4096 shapes included. A causal item
+// of query tile r covers keys 0..rows * (r + 1), so its mean is (N + rows) / 2.
+// Head dimensions the ping-pong kernel has no instance of (80, 96) take the
+// pipelined kernel. FLASH_ATTN_FWD_KERNEL=pipelined or =pingpong forces one (read at
+// every call; the ping-pong kernel serves d = 80 and 96 with its 128-wide instance).
+// inst is the smallest instance width (64, 80, 96 or 128) that holds the real head
+// dimension.
+int pick_unsplit(int64_t N, int inst, bool causal) {
+  const char* e = std::getenv("FLASH_ATTN_FWD_KERNEL");
+  if (e != nullptr && std::strcmp(e, "pingpong") == 0) return FA_FWD_KERNEL_PINGPONG;
+  if (e != nullptr && std::strcmp(e, "pipelined") == 0) return FA_FWD_KERNEL_PIPELINED;
+  if (inst != 64 && inst != 128) return FA_FWD_KERNEL_PIPELINED;
+  // (N + rows) / 2 without overflow for any N >= 0 (rows is even)
+  const int64_t keys = causal ? N / 2 + fa::rows_per_workgroup() / 2 : N;
+  return keys >= 4096 ? FA_FWD_KERNEL_PIPELINED : FA_FWD_KERNEL_PINGPONG;
+}
+
+int instance_width(int64_t d) { return d <= 64 ? 64 : d <= 80 ? 80 : d <= 96 ? 96 : 128; }
+
+// Calls with a key split always use the ping-pong kernel's split instance.
+hipError_t launch_unsplit(const fa::FwdArgs& a, bool fp16, int inst, bool causal, hipStream_t stream) {
+  return pick_unsplit(a.n, inst, causal) == FA_FWD_KERNEL_PIPELINED
+             ? fa::launch_fwd_sp(a, fp16, inst, causal, stream)
+             : fa::launch_fwd(a, fp16, inst <= 64 ? 64 : 128, causal, stream);
 }
 
 }  // namespace
 
-extern "C" int flash_attn_abi_version(void) { return 7; }
+extern "C" int flash_attn_abi_version(void) { return 8; }
 
 extern "C" const char* flash_attn_strerror(int status) {
   switch (status) {
@@ -340,10 +357,16 @@ extern "C" int flash_attn_fwd_strided(const void* q, const void* k, const void* 
   const int st = check_strided(q, k, v, o, lse, B, H, N, d, q_strides, k_strides, v_strides, o_strides,
                                lse_strides, causal, scale, dtype, &a, &empty);
   if (st != FA_OK || empty) return st;
-  const int inst = d <= 64 ? 64 : d <= 80 ? 80 : d <= 96 ? 96 : 128;
-  const hipError_t err =
-      launch_unsplit(a, dtype == FA_FP16, inst, causal == 1, static_cast<hipStream_t>(stream));
+  const hipError_t err = launch_unsplit(a, dtype == FA_FP16, instance_width(d), causal == 1,
+                                        static_cast<hipStream_t>(stream));
   return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+extern "C" int flash_attn_fwd_kernel(int64_t N, int64_t d, int causal) {
+  if (N < 0) return FA_ERR_SHAPE;
+  if (d < 8 || d > 128 || d % 8 != 0) return FA_ERR_HEADDIM;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  return pick_unsplit(N, instance_width(d), causal == 1);
 }
 
 extern "C" int flash_attn_fwd_splitkv_plan(int64_t B, int64_t H, int64_t N, int64_t d, int causal, int cus) {

@@ -273,9 +273,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_sp(FwdArgs a) {
   // rank j % q_tiles): consecutive items -- those the group's workgroups run at the
   // same time -- cover one or two slices, whose K/V tiles they then share through
   // the XCD's L2. Under a causal mask the snake then gives each workgroup ranks i
-  // and q_tiles - 1 - i only when q_tiles divides twice the group's workgroups, so
-  // other causal shapes keep rank-major order (rank j / hpx, slice j % hpx: every
-  // slice's heaviest tiles first). Causal rank 0 is the last, heaviest tile.
+  // and q_tiles - 1 - i only when q_tiles divides twice the group's workgroups and
+  // the items fill whole pairs of rounds, so other causal shapes keep rank-major
+  // order (rank j / hpx, slice j % hpx: every slice's heaviest tiles first). Causal
+  // rank 0 is the last, heaviest tile.
   const bool slice_major = a.slice_major != 0;
   auto item_split = [&](int j, int& slice, int& rank) {
     const int qd = (int)fastdiv((uint32_t)j, a.grp_mul, a.grp_shift);
@@ -1009,8 +1010,14 @@ hipError_t launch_fwd_sp(const FwdArgs& args, bool fp16, int d, bool causal, hip
     if (grid < 8) grid = 8;
   }
   a.grid = grid;
+  // slice-major order pairs each workgroup's causal ranks i and q_tiles - 1 - i only
+  // when q_tiles divides twice the group's workgroups and the group's items fill
+  // whole pairs of rounds; otherwise rank-major order (heaviest tiles of every slice
+  // first) balances better
   const int group_wgs = a.xcd_grouped ? grid >> 3 : grid;
-  a.slice_major = (!causal || (2 * group_wgs) % a.q_tiles == 0) ? 1 : 0;
+  const int64_t group_items = (int64_t)(a.xcd_grouped ? a.bh >> 3 : a.bh) * a.q_tiles;
+  a.slice_major =
+      (!causal || ((2 * group_wgs) % a.q_tiles == 0 && group_items % (2 * group_wgs) == 0)) ? 1 : 0;
   const FastDiv grp =
       make_fastdiv((uint32_t)(a.slice_major ? a.q_tiles : (a.xcd_grouped ? a.bh >> 3 : a.bh)));
   const FastDiv heads = make_fastdiv((uint32_t)a.heads);

@@ -39,6 +39,9 @@ typedef enum { FA_FP8_ROWS = 0, FA_FP8_KEYS_T = 1 } fa_fp8_layout;
  * flash_attn_fwd_fp8. */
 typedef enum { FA_FP8_E4M3 = 0, FA_FP8_E5M2 = 1 } fa_fp8_format;
 
+/* Forward kernels an unsplit call can run (flash_attn_fwd_kernel). */
+typedef enum { FA_FWD_KERNEL_PIPELINED = 1, FA_FWD_KERNEL_PINGPONG = 2 } fa_fwd_kernel;
+
 /* Return codes. Every check runs on the host before anything is launched. */
 typedef enum {
   FA_OK = 0,
@@ -376,12 +379,35 @@ int flash_attn_bwd_validate(const void* q, const void* k, const void* v, const v
                             int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
                             void* stream, int dtype);
 
+/*
+ * flash_attn_fwd_kernel -- which forward kernel flash_attn_fwd, flash_attn_fwd_strided
+ * and an unsplit flash_attn_fwd_splitkv call launch for sequence length N, head
+ * dimension d and mask `causal`. Both compute the same tiled online-softmax forward
+ * ("FlashAttention: optimize data movement before counting FLOPs", section 02, The
+ * mechanism) over 256-row query tiles; they differ in how the scores' softmax is
+ * overlapped with the matrix products. FA_FWD_KERNEL_PIPELINED software-pipelines
+ * each wave (scores of key tile t + 1 and the product of tile t - 1 around the
+ * softmax of tile t); FA_FWD_KERNEL_PINGPONG lets the two waves of a SIMD alternate.
+ * The pipelined kernel runs when a work item's mean key range, N without a mask and
+ * (N + 256) / 2 under the causal mask, is at least 4096 keys, and for d in 65..96
+ * (80- and 96-wide instances); the ping-pong kernel otherwise. The environment
+ * variable FLASH_ATTN_FWD_KERNEL, read at every call, forces one: "pipelined" or
+ * "pingpong" (then d in 65..96 runs the ping-pong kernel's 128-wide instance).
+ * N     : sequence length, >= 0 (else FA_ERR_SHAPE).
+ * d     : head dimension, a multiple of 8 in 8..128 (else FA_ERR_HEADDIM).
+ * causal: 0 or 1 (else FA_ERR_ARG).
+ * Returns FA_FWD_KERNEL_PIPELINED or FA_FWD_KERNEL_PINGPONG, or the negative status.
+ * Makes no HIP call and keeps no state.
+ */
+int flash_attn_fwd_kernel(int64_t N, int64_t d, int causal);
+
 /* Static, never-freed description of a status code (unknown codes included). */
 const char* flash_attn_strerror(int status);
 
-/* ABI version of this header, currently 7 (1: forward only; 2: + backward;
+/* ABI version of this header, currently 8 (1: forward only; 2: + backward;
  * 3: + key-split forward; 4: + strided forward; 5: + FP8 quantization and forward;
- * 6: + key-split forward without a caller workspace; 7: FP8 format argument, E5M2). */
+ * 6: + key-split forward without a caller workspace; 7: FP8 format argument, E5M2;
+ * 8: + forward kernel query). */
 int flash_attn_abi_version(void);
 
 #ifdef __cplusplus

@@ -19,6 +19,7 @@
 // ---- stubs of the device side ----
 namespace {
 int g_launches = 0;
+int g_kernel = 0;  // forward kernel of the last unsplit launch (FA_FWD_KERNEL_*)
 fa::FwdArgs g_fwd;
 }  // namespace
 
@@ -27,12 +28,14 @@ int rows_per_workgroup() { return 256; }
 int keys_per_tile() { return 64; }
 int device_cus() { return 256; }
 hipError_t launch_fwd(const FwdArgs& a, bool, int, bool, hipStream_t) {
+  if (a.splits <= 1) g_kernel = FA_FWD_KERNEL_PINGPONG;
   g_fwd = a;
   ++g_launches;
   return hipSuccess;
 }
 hipError_t launch_fwd_sp(const FwdArgs& a, bool, int d, bool, hipStream_t) {
   if (d != 64 && d != 80 && d != 96 && d != 128) std::abort();
+  g_kernel = FA_FWD_KERNEL_PIPELINED;
   g_fwd = a;
   ++g_launches;
   return hipSuccess;
@@ -106,7 +109,13 @@ void known_cases() {
   const uint64_t GB = 1ull << 30;
   void *q = base, *k = base + GB, *v = base + 2 * GB, *o = base + 3 * GB;
   float* lse = reinterpret_cast<float*>(base + 4 * GB);
-  CHECK(flash_attn_abi_version() == 7);
+  CHECK(flash_attn_abi_version() == 8);
+  CHECK(flash_attn_fwd(q, k, v, o, lse, 2, 32, 4096, 128, 1, 0.088f, nullptr, FA_BF16) == FA_OK);
+  CHECK(g_kernel == FA_FWD_KERNEL_PINGPONG && flash_attn_fwd_kernel(4096, 128, 1) == FA_FWD_KERNEL_PINGPONG);
+  CHECK(flash_attn_fwd(q, k, v, o, lse, 1, 32, 16384, 128, 1, 0.088f, nullptr, FA_BF16) == FA_OK);
+  CHECK(g_kernel == FA_FWD_KERNEL_PIPELINED && flash_attn_fwd_kernel(16384, 128, 1) == FA_FWD_KERNEL_PIPELINED);
+  CHECK(flash_attn_fwd_kernel(-1, 128, 1) == FA_ERR_SHAPE && flash_attn_fwd_kernel(1, 130, 1) == FA_ERR_HEADDIM);
+  CHECK(flash_attn_fwd_kernel(1, 128, 2) == FA_ERR_ARG);
   CHECK(flash_attn_fwd(q, k, v, o, lse, 2, 32, 4096, 128, 1, 0.088f, nullptr, FA_BF16) == FA_OK);
   CHECK(g_fwd.bh == 64 && g_fwd.n == 4096 && g_fwd.q_tiles == 16 && g_fwd.xcd_grouped == 1);
   CHECK(g_fwd.q_ext == 4096u * 128u * 2u && g_fwd.k_sh == 4096 * 128);
@@ -163,7 +172,12 @@ void fuzz(int rounds) {
     void *q = buf(0), *k = buf(1), *v = buf(2), *o = buf(3);
     float* lse = static_cast<float*>(buf(4));
     flash_attn_fwd_validate(q, k, v, o, lse, B, H, N, d, causal, scale, nullptr, dtype);
-    flash_attn_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, nullptr, dtype);
+    g_kernel = 0;
+    const int fst = flash_attn_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, nullptr, dtype);
+    const int kern = flash_attn_fwd_kernel(N, d, causal);
+    // a call that launched ran the kernel the query names
+    if (fst == FA_OK && g_kernel != 0) CHECK(g_kernel == kern);
+    if (fst == FA_OK && B > 0 && H > 0 && N > 0) CHECK(g_kernel == kern);
     int64_t s4[4][3], ls[2];
     for (auto& t : s4)
       for (auto& x : t) x = any_size();

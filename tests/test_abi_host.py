@@ -35,7 +35,7 @@ def test_library_loads_and_exports_header_symbols():
     assert os.path.exists(LIB_PATH), "build the library first (__graft_entry__.build())"
     names = _declared_functions()
     assert names == ["flash_attn_abi_version", "flash_attn_bwd", "flash_attn_bwd_validate", "flash_attn_fwd",
-                     "flash_attn_fwd_fp8", "flash_attn_fwd_fp8_validate",
+                     "flash_attn_fwd_fp8", "flash_attn_fwd_fp8_validate", "flash_attn_fwd_kernel",
                      "flash_attn_fwd_splitkv", "flash_attn_fwd_splitkv_noalloc", "flash_attn_fwd_splitkv_plan",
                      "flash_attn_fwd_splitkv_validate",
                      "flash_attn_fwd_splitkv_workspace_size", "flash_attn_fwd_strided",
@@ -50,7 +50,7 @@ def test_library_loads_and_exports_header_symbols():
 
 
 def test_abi_version_and_strerror():
-    assert fa.flash_attn_abi_version() == 7
+    assert fa.flash_attn_abi_version() == 8
     codes = [fa.FA_OK, fa.FA_ERR_NULL, fa.FA_ERR_SHAPE, fa.FA_ERR_HEADDIM, fa.FA_ERR_DTYPE,
              fa.FA_ERR_SCALE, fa.FA_ERR_ALIGN, fa.FA_ERR_ALIAS, fa.FA_ERR_HIP, fa.FA_ERR_ARG,
              fa.FA_ERR_WORKSPACE, fa.FA_ERR_STRIDE, fa.FA_ERR_SCRATCH]
@@ -465,3 +465,37 @@ def test_fp8_accepts_and_empty():
     assert _native.validate_fp8_raw(*_fargs(fmt=fa.FA_FP8_E5M2)) == fa.FA_OK
     assert _native.fp8_raw(*_fargs(q8=None, k8=None, v8t=None, qs=None, ks=None, vs=None, o=None, lse=None,
                                    H=0)) == fa.FA_OK
+
+
+# (N, d, causal, kernel): the pipelined kernel from a mean key range of 4096 per
+# 256-row item (N without a mask, (N + 256) / 2 under it) and for d in 65..96;
+# the ping-pong kernel otherwise
+PIPE, PING = _native.FA_FWD_KERNEL_PIPELINED, _native.FA_FWD_KERNEL_PINGPONG
+
+
+@pytest.mark.parametrize("N,d,causal,want", [
+    (0, 64, 0, PING), (256, 64, 0, PING), (4095, 128, 0, PING), (4096, 128, 0, PIPE), (4099, 128, 0, PIPE),
+    (4096, 128, 1, PING), (7935, 128, 1, PING), (7936, 128, 1, PIPE), (16384, 128, 1, PIPE),
+    (1024, 56, 0, PING), (300, 72, 1, PIPE), (300, 80, 0, PIPE), (300, 88, 1, PIPE), (300, 96, 0, PIPE),
+    (300, 104, 0, PING), (8192, 8, 0, PIPE)])
+def test_fwd_kernel_choice(monkeypatch, N, d, causal, want):
+    monkeypatch.delenv("FLASH_ATTN_FWD_KERNEL", raising=False)
+    assert _native.fwd_kernel(N, d, causal) == want
+    assert fa.flash_attn_fwd_kernel(N, d, bool(causal)) == ("pipelined" if want == PIPE else "pingpong")
+
+
+def test_fwd_kernel_forced_and_rejects(monkeypatch):
+    monkeypatch.setenv("FLASH_ATTN_FWD_KERNEL", "pingpong")
+    assert _native.fwd_kernel(16384, 128, 1) == PING
+    assert _native.fwd_kernel(300, 80, 0) == PING
+    monkeypatch.setenv("FLASH_ATTN_FWD_KERNEL", "pipelined")
+    assert _native.fwd_kernel(256, 64, 0) == PIPE
+    monkeypatch.setenv("FLASH_ATTN_FWD_KERNEL", "other")   # unknown names are ignored
+    assert _native.fwd_kernel(256, 64, 0) == PING
+    monkeypatch.delenv("FLASH_ATTN_FWD_KERNEL")
+    assert _native.fwd_kernel(-1, 64, 0) == fa.FA_ERR_SHAPE
+    for d in (0, 7, 12, 136):
+        assert _native.fwd_kernel(256, d, 0) == fa.FA_ERR_HEADDIM
+    assert _native.fwd_kernel(256, 64, 2) == fa.FA_ERR_ARG
+    with pytest.raises(fa.FlashAttnError):
+        fa.flash_attn_fwd_kernel(256, 12)

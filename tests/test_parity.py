@@ -6,12 +6,14 @@ the 16-bit outputs exactly and compares element by element with oracle.dense on
 the same bytes, with the tolerances of tests/_parity.py.
 
 * Small shapes: full outputs, sizes that span several 128-row query tiles and
-  64-row key tiles, with ragged tails, N = 1 and N = 3, both dtypes, both masks.
+  64-row key tiles, with ragged tails, N = 1 and N = 3, both dtypes, both masks,
+  each through both forward kernels (FLASH_ATTN_FWD_KERNEL forces one).
 * The five workloads at full size, in the same launch configuration the
   benchmark times: complete outputs where the oracle is quick (the 256- and
   1024-token workloads) and otherwise sampled rows of every (batch, head) --
   first/last rows, tile and wave boundaries, the ragged end and random rows --
-  plus complete heads; each with the workload seed and seed + 100.
+  plus complete heads; each with the workload seed and seed + 100 through the
+  kernel the call picks, and with the workload seed through the other kernel.
 * Properties: the worked example of the tokenlab note zero-padded to d = 64,
   V = 1, Q = 0, the causal prefix property (bitwise), determinism, a side stream,
   empty problems and very large logits.
@@ -72,14 +74,14 @@ SMALL_SHAPES = [(1, 1, 1, 64), (1, 1, 3, 128), (1, 2, 63, 64), (1, 1, 64, 128), 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("dtype", [inputs.BF16, inputs.FP16])
 @pytest.mark.parametrize("shape", SMALL_SHAPES)
-def test_small_shapes_full(fa, shape, dtype, causal):
+def test_small_shapes_full(fa, fwd_kernel, shape, dtype, causal):
     seed = 1000 + 7 * SMALL_SHAPES.index(shape) + (3 if causal else 0) + (1 if dtype == inputs.FP16 else 0)
     qb, kb, vb = inputs.draw_qkv(shape, dtype, 1.0, seed)
     scale = inputs.default_scale(shape[-1])
     o, lse = _run_gpu(fa, qb, kb, vb, dtype, causal, scale)
     ro, rl = _oracle(qb, kb, vb, dtype, causal, scale)
     m = metrics(o, lse, ro, rl, dtype)
-    _log(f"small {shape} {dtype} causal={causal}: {m}")
+    _log(f"small {fwd_kernel} {shape} {dtype} causal={causal}: {m}")
     assert_parity(m, f"{shape} {dtype} causal={causal}")
 
 
@@ -114,13 +116,21 @@ EXTRA = {"llama7b_b2_h32_n4096_d128_noncausal": inputs.Workload(
 CASES += [(name, c) for name, w in EXTRA.items() for c in w.causal]
 
 
-@pytest.mark.parametrize("seed_offset", [0, 100])
+@pytest.mark.parametrize("seed_offset,kernel", [(0, "picked"), (100, "picked"), (0, "other")])
 @pytest.mark.parametrize("name,causal", CASES)
-def test_workload_parity(fa, name, causal, seed_offset):
-    """Full size, in the launch configuration the benchmark times: complete outputs
-    where the oracle is quick, otherwise at least one row of every work item
-    (slice, 256-row query tile) of every slice, plus complete slices."""
+def test_workload_parity(fa, monkeypatch, name, causal, seed_offset, kernel):
+    """Full size, in the launch configuration the benchmark times (the kernel the
+    call picks), and through the other forward kernel: complete outputs where the
+    oracle is quick, otherwise at least one row of every work item (slice, 256-row
+    query tile) of every slice, plus complete slices."""
     w = inputs.WORKLOADS[name] if name in inputs.WORKLOADS else EXTRA[name]
+    monkeypatch.delenv("FLASH_ATTN_FWD_KERNEL", raising=False)
+    picked = fa._native.fwd_kernel(w.N, w.d, causal)
+    assert picked in (fa._native.FA_FWD_KERNEL_PIPELINED, fa._native.FA_FWD_KERNEL_PINGPONG)
+    if kernel == "other":
+        monkeypatch.setenv("FLASH_ATTN_FWD_KERNEL",
+                           "pingpong" if picked == fa._native.FA_FWD_KERNEL_PIPELINED else "pipelined")
+    _log(f"workload {name} causal={causal}: kernel {kernel} (picked {picked})")
     t0 = time.time()
     qb, kb, vb = inputs.workload_qkv(w, seed_offset)
     scale = inputs.default_scale(w.d)
@@ -168,14 +178,14 @@ MULTI_ITEM_SHAPES = [(8, 32, 512, 128), (16, 32, 512, 64), (6, 32, 704, 128)]
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("dtype", [inputs.BF16, inputs.FP16])
 @pytest.mark.parametrize("shape", MULTI_ITEM_SHAPES)
-def test_multi_item_workgroups_full(fa, shape, dtype, causal):
+def test_multi_item_workgroups_full(fa, fwd_kernel, shape, dtype, causal):
     seed = 2000 + 11 * MULTI_ITEM_SHAPES.index(shape) + (3 if causal else 0) + (1 if dtype == inputs.FP16 else 0)
     qb, kb, vb = inputs.draw_qkv(shape, dtype, 1.0, seed)
     scale = inputs.default_scale(shape[-1])
     o, lse = _run_gpu(fa, qb, kb, vb, dtype, causal, scale)
     ro, rl = _oracle(qb, kb, vb, dtype, causal, scale)
     m = metrics(o, lse, ro, rl, dtype)
-    _log(f"multi-item {shape} {dtype} causal={causal}: {m}")
+    _log(f"multi-item {fwd_kernel} {shape} {dtype} causal={causal}: {m}")
     assert_parity(m, f"{shape} {dtype} causal={causal}")
 
 
@@ -309,17 +319,23 @@ def test_launch_log_names_the_instance():
     import subprocess
 
     code = (
-        "import torch, exact_attention_flash_amd as fa\n"
+        "import os, torch, exact_attention_flash_amd as fa\n"
         "q = torch.randn(1, 8, 300, 128, device='cuda', dtype=torch.bfloat16)\n"
+        "o, lse = fa.forward(q, q, q, causal=True)\n"
+        "os.environ['FLASH_ATTN_FWD_KERNEL'] = 'pipelined'\n"
         "o, lse = fa.forward(q, q, q, causal=True)\n"
         "fa.backward(q, q, q, o, lse, torch.randn_like(q), causal=True)\n"
         "torch.cuda.synchronize()\n")
     env = dict(os.environ, FLASH_ATTN_LOG="1")
+    env.pop("FLASH_ATTN_FWD_KERNEL", None)
     res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, timeout=120)
     assert res.returncode == 0, res.stderr[-2000:]
     _log(res.stderr.strip())
-    assert "flash_attn: fwd_sp<bf16, 128, causal> grid 16 x 512, 16 items" in res.stderr
-    assert "bwd_dkdv<bf16, 128, causal>" in res.stderr
+    lines = [l for l in res.stderr.splitlines() if l.startswith("flash_attn: ")]
+    # 300 keys per item: the ping-pong kernel; then the pipelined one, forced
+    assert lines[0].startswith("flash_attn: fwd_pingpong<bf16, 128, causal, whole> grid "), lines
+    assert lines[1].startswith("flash_attn: fwd_sp<bf16, 128, causal> grid 16 x 512, 16 items"), lines
+    assert any("bwd_dkdv<bf16, 128, causal>" in l for l in lines[2:]), lines
 
 
 @pytest.mark.parametrize("pattern", ["rising", "first_spike"])

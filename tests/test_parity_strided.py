@@ -3,7 +3,7 @@ not 64 or 128, against the float64 oracle (tolerances of tests/_parity.py).
 
 * Head dimensions d in {8, 24, 40, 56, 72, 80, 96, 120} (multiples of 8, masked up to
   the 64- or 128-wide kernel as "6.1 FlashAttention V1 in detail", §8.3 masks
-  BLOCK_D > D), both dtypes and masks, ragged N.
+  BLOCK_D > D), both dtypes and masks, ragged N, through both forward kernels.
 * Layouts: q, k, v as views of one packed [B, N, 3, H, d] projection output; o written
   into a [B, N, H, d] tensor; padded rows whose padding holds NaN (never read: a read
   would poison the result); padded output rows and lse rows whose padding must keep
@@ -63,7 +63,7 @@ def _oracle(bits, dtype, causal, scale):
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("dtype", [inputs.BF16, inputs.FP16])
 @pytest.mark.parametrize("d", [8, 24, 40, 56, 72, 80, 88, 96, 120])
-def test_head_dims(fa, d, dtype, causal):
+def test_head_dims(fa, fwd_kernel, d, dtype, causal):
     shape = (2, 2, 300, d)
     scale = _scale(d)
     bits = inputs.draw_qkv(shape, dtype, 1.0, 700 + d + (1 if causal else 0))
@@ -72,7 +72,7 @@ def test_head_dims(fa, d, dtype, causal):
     torch.cuda.synchronize()
     ro, rl = _oracle(bits, dtype, causal, scale)
     m = metrics(_o64(o, dtype), lse.double().cpu().numpy(), ro, rl, dtype)
-    _log(f"strided d={d} {dtype} causal={causal}: {m}")
+    _log(f"strided {fwd_kernel} d={d} {dtype} causal={causal}: {m}")
     assert_parity(m, f"d={d} {dtype} causal={causal}")
 
 
@@ -162,7 +162,7 @@ def test_contiguous_strided_equals_plain(fa, d, causal):
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("d", [80, 96])
-def test_head_dims_multi_item_workgroups(fa, d, causal):
+def test_head_dims_multi_item_workgroups(fa, fwd_kernel, d, causal):
     """The 80- and 96-wide instances with several items per workgroup (4*32 slices of
     three 256-row query tiles, the last ragged: 384 items on at most 256 workgroups),
     compared in full."""
@@ -174,7 +174,7 @@ def test_head_dims_multi_item_workgroups(fa, d, causal):
     torch.cuda.synchronize()
     ro, rl = _oracle(bits, dtype, causal, scale)
     m = metrics(_o64(o, dtype), lse.double().cpu().numpy(), ro, rl, dtype)
-    _log(f"strided d={d} multi-item causal={causal}: {m}")
+    _log(f"strided {fwd_kernel} d={d} multi-item causal={causal}: {m}")
     assert_parity(m, f"d={d} multi-item causal={causal}")
 
 
