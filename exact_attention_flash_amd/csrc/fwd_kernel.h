@@ -34,8 +34,8 @@ struct FwdArgs {
   int64_t q_sb, q_sh, k_sb, k_sh, v_sb, v_sh, o_sb, o_sh, l_sb, l_sh;
   int q_sn, k_sn, v_sn, o_sn;
   uint32_t q_ext, k_ext, v_ext;
-  // filled by the launcher of the software-pipelined kernel: the item order
-  // (1: slice-major, 0: rank-major) and multiply-high / shift pairs that divide by
+  // filled by the launchers: the item order (1: slice-major, 0: rank-major); and,
+  // for the software-pipelined kernel, multiply-high / shift pairs that divide by
   // its group divisor (q_tiles, or the slices per group) and by heads
   int slice_major;
   uint32_t grp_mul, grp_shift, heads_mul, heads_shift;

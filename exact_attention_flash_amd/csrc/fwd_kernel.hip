@@ -136,12 +136,16 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
   const int l32 = lane & 31;
 
   // ---- persistent schedule ----
-  // Work items are (slice, query tile) pairs, ranked heaviest causal query tile
-  // first. With xcd_grouped, the workgroups of XCD x (blockIdx % 8 == x) own slices
-  // [x*hpx, (x+1)*hpx), so all query tiles of a slice share K/V through one L2.
-  // Workgroup k of a group of size G takes the items k, 2G-1-k, 2G+k, 4G-1-k, ...
-  // of its group's ranked list (snake order), which gives every workgroup the same
-  // causal work when the list is a whole number of rounds.
+  // Work items are (slice, query tile) pairs. With xcd_grouped, the workgroups of
+  // XCD x (blockIdx % 8 == x) own slices [x*hpx, (x+1)*hpx), so all query tiles of
+  // a slice share K/V through one L2. Workgroup k of a group of size G takes the
+  // items k, 2G-1-k, 2G+k, 4G-1-k, ... of its group's list (snake order). The list
+  // is slice-major when a.slice_major is set (no key split): the items a group's
+  // workgroups run at the same time cover one or two slices, whose K/V then stay in
+  // the XCD's L2, and the snake pairs causal ranks i and q_tiles - 1 - i; the host
+  // sets it only when those pairs fill whole rounds (or without a mask). Otherwise
+  // the list is rank-major (every slice's rank 0, then rank 1, ...): the heaviest
+  // causal query tiles first, balanced by the snake over whole rounds.
   const int bid = blockIdx.x;
   int wg_k, wg_n, hpx, bh_base;
   if (a.xcd_grouped) {
@@ -169,10 +173,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
     const int j = r * wg_n + ((r & 1) ? wg_n - 1 - wg_k : wg_k);
     return j < n_items ? j : -1;
   };
-  // item j: slice j % hpx; query-tile rank and key split from j / hpx (the splits
-  // of one query tile are adjacent in the ranked list)
-  auto item_bh = [&](int j) { return bh_base + j % hpx; };
-  auto item_rank = [&](int j) { return SPLIT ? (j / hpx) / splits : j / hpx; };
+  // item j, slice-major: slice j / q_tiles, rank j % q_tiles. Rank-major: slice
+  // j % hpx; query-tile rank and key split from j / hpx (the splits of one query
+  // tile are adjacent in the list). Causal rank 0 is the last, heaviest query tile.
+  const bool slice_major = !SPLIT && a.slice_major != 0;
+  auto item_bh = [&](int j) { return bh_base + (slice_major ? j / a.q_tiles : j % hpx); };
+  auto item_rank = [&](int j) {
+    return slice_major ? j % a.q_tiles : SPLIT ? (j / hpx) / splits : j / hpx;
+  };
   auto item_split = [&](int j) { return SPLIT ? (j / hpx) % splits : 0; };
   auto item_q0 = [&](int j) { return (CAUSAL ? (a.q_tiles - 1 - item_rank(j)) : item_rank(j)) * kBM; };
   // key tiles visited by a query tile starting at q0 (causal: up to its last row)
@@ -494,19 +502,15 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
       // (the raised issue priority of the matrix phase starts before the loads, so
       // that the cursor work of the wave about to feed the matrix pipe is not held
       // up by the other wave's softmax)
-      if (grp == 0) {
-        __builtin_amdgcn_s_setprio(1);
-        if (i < n_tiles) issue_next();
-        if (q_in_flight) issue_q(next_j);
-        mfma_phase(i);
-        softmax_phase(i);
-      } else {
-        softmax_phase(i - 1);
-        __builtin_amdgcn_s_setprio(1);
-        if (i < n_tiles) issue_next();
-        if (q_in_flight) issue_q(next_j);
-        mfma_phase(i);
-      }
+      // Only the softmax calls sit under the group test: the compiler cannot tell
+      // that it is uniform per wave, and the stream cursor must be updated outside
+      // such branches to stay in scalar registers.
+      if (grp != 0) softmax_phase(i - 1);
+      __builtin_amdgcn_s_setprio(1);
+      if (i < n_tiles) issue_next();
+      if (q_in_flight) issue_q(next_j);
+      mfma_phase(i);
+      if (grp == 0) softmax_phase(i);
       // tile i+1 must have landed (every wave waits for its own loads) before the
       // barrier that publishes it; only the next item's Q may still be in flight
       if (i + 1 < n_tiles) {
@@ -615,8 +619,9 @@ __global__ __launch_bounds__(256) void merge_splits(FwdArgs a) {
 
 template <bool FP16, int D, bool CAUSAL>
 hipError_t launch_one(const FwdArgs& a, hipStream_t stream) {
-  launch_log("fwd_pingpong<%s, %d, %s, %s> grid %d x %d, %d splits", dtype_name(FP16), D, CAUSAL ? "causal" : "full",
-             a.splits > 1 ? "split" : "whole", a.grid, kThreads, a.splits);
+  launch_log("fwd_pingpong<%s, %d, %s, %s> grid %d x %d, %d splits, %s order", dtype_name(FP16), D,
+             CAUSAL ? "causal" : "full", a.splits > 1 ? "split" : "whole", a.grid, kThreads, a.splits,
+             a.slice_major ? "slice-major" : "rank-major");
   if (a.splits > 1) {
     hipLaunchKernelGGL((fwd_pingpong<FP16, D, CAUSAL, true>), dim3(a.grid), dim3(kThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
@@ -668,6 +673,12 @@ hipError_t launch_fwd(const FwdArgs& args, bool fp16, int d, bool causal, hipStr
     if (grid < 8) grid = 8;
   }
   a.grid = grid;
+  // slice-major item order (unsplit only) where the snake's causal pairs fill whole
+  // rounds of the schedule group
+  const int64_t group_wgs = a.xcd_grouped ? grid >> 3 : grid;
+  const int64_t group_items = (int64_t)(a.xcd_grouped ? a.bh >> 3 : a.bh) * a.q_tiles;
+  a.slice_major = a.splits <= 1 && (!causal || ((2 * group_wgs) % a.q_tiles == 0 &&
+                                                group_items % (2 * group_wgs) == 0));
   if (fp16) {
     if (d == 64) return causal ? launch_one<true, 64, true>(a, stream) : launch_one<true, 64, false>(a, stream);
     return causal ? launch_one<true, 128, true>(a, stream) : launch_one<true, 128, false>(a, stream);
