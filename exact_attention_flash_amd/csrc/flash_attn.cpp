@@ -25,33 +25,30 @@ bool overlaps(const void* a, uint64_t an, const void* b, uint64_t bn) {
 bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
 // Forward kernel of a call without a key split. The software-pipelined kernel
-// (fwd_sp.hip) overlaps each wave's softmax with its own products but pays more per
-// work item to fill and drain its pipeline; the ping-pong kernel (fwd_kernel.hip)
-// overlaps the two waves of a SIMD and starts items cheaply. Measured on one MI355X
-// over 20 shapes, the pipelined kernel is ahead (0.6-2.4%) once a work item's mean
-// key range reaches 4096 keys (non-causal N >= 4096, causal N >= 8K), and level or
-// behind (up to 15%) below that, the causal N = 4096 shapes included. A causal item
-// of query tile r covers keys 0..rows * (r + 1), so its mean is (N + rows) / 2.
-// Head dimensions the ping-pong kernel has no instance of (80, 96) take the
-// pipelined kernel. FLASH_ATTN_FWD_KERNEL=pipelined or =pingpong forces one (read at
-// every call; the ping-pong kernel serves d = 80 and 96 with its 128-wide instance).
-// inst is the smallest instance width (64, 80, 96 or 128) that holds the real head
-// dimension.
-int pick_unsplit(int64_t N, int inst, bool causal) {
+// (fwd_sp.hip) overlaps each wave's softmax with its own products; the ping-pong
+// kernel (fwd_kernel.hip) overlaps the two waves of a SIMD and starts work items
+// more cheaply. Measured on one MI355X (same-process A/B over 28 shapes), the
+// ping-pong kernel is 2-15% faster wherever a work item spans fewer than 4096 keys
+// (the causal B2 H32 N4096 d128 workload included) and level (within +-2%, either
+// way) on longer ones, so it serves head dimensions up to 64 and 97..128 (its 64-
+// and 128-wide instances). Head dimensions 65..96 take the pipelined kernel's 80- and
+// 96-wide instances rather than the ping-pong kernel's 128-wide one with its
+// zero-padded columns. FLASH_ATTN_FWD_KERNEL=pipelined or =pingpong forces one
+// (read at every call; the ping-pong kernel serves d = 65..96 with its 128-wide
+// instance). inst is the smallest instance width (64, 80, 96 or 128) that holds the
+// real head dimension.
+int pick_unsplit(int inst) {
   const char* e = std::getenv("FLASH_ATTN_FWD_KERNEL");
   if (e != nullptr && std::strcmp(e, "pingpong") == 0) return FA_FWD_KERNEL_PINGPONG;
   if (e != nullptr && std::strcmp(e, "pipelined") == 0) return FA_FWD_KERNEL_PIPELINED;
-  if (inst != 64 && inst != 128) return FA_FWD_KERNEL_PIPELINED;
-  // (N + rows) / 2 without overflow for any N >= 0 (rows is even)
-  const int64_t keys = causal ? N / 2 + fa::rows_per_workgroup() / 2 : N;
-  return keys >= 4096 ? FA_FWD_KERNEL_PIPELINED : FA_FWD_KERNEL_PINGPONG;
+  return inst == 64 || inst == 128 ? FA_FWD_KERNEL_PINGPONG : FA_FWD_KERNEL_PIPELINED;
 }
 
 int instance_width(int64_t d) { return d <= 64 ? 64 : d <= 80 ? 80 : d <= 96 ? 96 : 128; }
 
 // Calls with a key split always use the ping-pong kernel's split instance.
 hipError_t launch_unsplit(const fa::FwdArgs& a, bool fp16, int inst, bool causal, hipStream_t stream) {
-  return pick_unsplit(a.n, inst, causal) == FA_FWD_KERNEL_PIPELINED
+  return pick_unsplit(inst) == FA_FWD_KERNEL_PIPELINED
              ? fa::launch_fwd_sp(a, fp16, inst, causal, stream)
              : fa::launch_fwd(a, fp16, inst <= 64 ? 64 : 128, causal, stream);
 }
@@ -366,7 +363,7 @@ extern "C" int flash_attn_fwd_kernel(int64_t N, int64_t d, int causal) {
   if (N < 0) return FA_ERR_SHAPE;
   if (d < 8 || d > 128 || d % 8 != 0) return FA_ERR_HEADDIM;
   if (causal != 0 && causal != 1) return FA_ERR_ARG;
-  return pick_unsplit(N, instance_width(d), causal == 1);
+  return pick_unsplit(instance_width(d));
 }
 
 extern "C" int flash_attn_fwd_splitkv_plan(int64_t B, int64_t H, int64_t N, int64_t d, int causal, int cus) {

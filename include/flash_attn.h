@@ -388,11 +388,12 @@ int flash_attn_bwd_validate(const void* q, const void* k, const void* v, const v
  * overlapped with the matrix products. FA_FWD_KERNEL_PIPELINED software-pipelines
  * each wave (scores of key tile t + 1 and the product of tile t - 1 around the
  * softmax of tile t); FA_FWD_KERNEL_PINGPONG lets the two waves of a SIMD alternate.
- * The pipelined kernel runs when a work item's mean key range, N without a mask and
- * (N + 256) / 2 under the causal mask, is at least 4096 keys, and for d in 65..96
- * (80- and 96-wide instances); the ping-pong kernel otherwise. The environment
- * variable FLASH_ATTN_FWD_KERNEL, read at every call, forces one: "pipelined" or
- * "pingpong" (then d in 65..96 runs the ping-pong kernel's 128-wide instance).
+ * The ping-pong kernel serves d <= 64 and d in 97..128 (its 64- and 128-wide
+ * instances); the pipelined kernel serves d in 65..96 (80- and 96-wide instances).
+ * The choice does not depend on N or the mask today; both arguments are checked
+ * and kept so that it may. The environment variable FLASH_ATTN_FWD_KERNEL, read at
+ * every call, forces one: "pipelined" or "pingpong" (then d in 65..96 runs the
+ * ping-pong kernel's 128-wide instance).
  * N     : sequence length, >= 0 (else FA_ERR_SHAPE).
  * d     : head dimension, a multiple of 8 in 8..128 (else FA_ERR_HEADDIM).
  * causal: 0 or 1 (else FA_ERR_ARG).

@@ -113,7 +113,8 @@ void known_cases() {
   CHECK(flash_attn_fwd(q, k, v, o, lse, 2, 32, 4096, 128, 1, 0.088f, nullptr, FA_BF16) == FA_OK);
   CHECK(g_kernel == FA_FWD_KERNEL_PINGPONG && flash_attn_fwd_kernel(4096, 128, 1) == FA_FWD_KERNEL_PINGPONG);
   CHECK(flash_attn_fwd(q, k, v, o, lse, 1, 32, 16384, 128, 1, 0.088f, nullptr, FA_BF16) == FA_OK);
-  CHECK(g_kernel == FA_FWD_KERNEL_PIPELINED && flash_attn_fwd_kernel(16384, 128, 1) == FA_FWD_KERNEL_PIPELINED);
+  CHECK(g_kernel == FA_FWD_KERNEL_PINGPONG && flash_attn_fwd_kernel(16384, 128, 1) == FA_FWD_KERNEL_PINGPONG);
+  CHECK(flash_attn_fwd_kernel(300, 80, 1) == FA_FWD_KERNEL_PIPELINED);
   CHECK(flash_attn_fwd_kernel(-1, 128, 1) == FA_ERR_SHAPE && flash_attn_fwd_kernel(1, 130, 1) == FA_ERR_HEADDIM);
   CHECK(flash_attn_fwd_kernel(1, 128, 2) == FA_ERR_ARG);
   CHECK(flash_attn_fwd(q, k, v, o, lse, 2, 32, 4096, 128, 1, 0.088f, nullptr, FA_BF16) == FA_OK);

@@ -467,17 +467,15 @@ def test_fp8_accepts_and_empty():
                                    H=0)) == fa.FA_OK
 
 
-# (N, d, causal, kernel): the pipelined kernel from a mean key range of 4096 per
-# 256-row item (N without a mask, (N + 256) / 2 under it) and for d in 65..96;
-# the ping-pong kernel otherwise
+# (N, d, causal, kernel): the ping-pong kernel for d <= 64 and 97..128, the
+# pipelined kernel for d in 65..96, at any N and mask
 PIPE, PING = _native.FA_FWD_KERNEL_PIPELINED, _native.FA_FWD_KERNEL_PINGPONG
 
 
 @pytest.mark.parametrize("N,d,causal,want", [
-    (0, 64, 0, PING), (256, 64, 0, PING), (4095, 128, 0, PING), (4096, 128, 0, PIPE), (4099, 128, 0, PIPE),
-    (4096, 128, 1, PING), (7935, 128, 1, PING), (7936, 128, 1, PIPE), (16384, 128, 1, PIPE),
-    (1024, 56, 0, PING), (300, 72, 1, PIPE), (300, 80, 0, PIPE), (300, 88, 1, PIPE), (300, 96, 0, PIPE),
-    (300, 104, 0, PING), (8192, 8, 0, PIPE)])
+    (0, 64, 0, PING), (256, 64, 0, PING), (4096, 128, 0, PING), (4096, 128, 1, PING), (16384, 128, 1, PING),
+    (65536, 128, 0, PING), (1024, 56, 0, PING), (300, 72, 1, PIPE), (300, 80, 0, PIPE), (300, 88, 1, PIPE),
+    (300, 96, 0, PIPE), (16384, 96, 1, PIPE), (300, 104, 0, PING), (8192, 8, 0, PING)])
 def test_fwd_kernel_choice(monkeypatch, N, d, causal, want):
     monkeypatch.delenv("FLASH_ATTN_FWD_KERNEL", raising=False)
     assert _native.fwd_kernel(N, d, causal) == want
@@ -491,7 +489,7 @@ def test_fwd_kernel_forced_and_rejects(monkeypatch):
     monkeypatch.setenv("FLASH_ATTN_FWD_KERNEL", "pipelined")
     assert _native.fwd_kernel(256, 64, 0) == PIPE
     monkeypatch.setenv("FLASH_ATTN_FWD_KERNEL", "other")   # unknown names are ignored
-    assert _native.fwd_kernel(256, 64, 0) == PING
+    assert _native.fwd_kernel(256, 64, 0) == PING and _native.fwd_kernel(256, 80, 0) == PIPE
     monkeypatch.delenv("FLASH_ATTN_FWD_KERNEL")
     assert _native.fwd_kernel(-1, 64, 0) == fa.FA_ERR_SHAPE
     for d in (0, 7, 12, 136):

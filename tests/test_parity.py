@@ -332,7 +332,7 @@ def test_launch_log_names_the_instance():
     assert res.returncode == 0, res.stderr[-2000:]
     _log(res.stderr.strip())
     lines = [l for l in res.stderr.splitlines() if l.startswith("flash_attn: ")]
-    # 300 keys per item: the ping-pong kernel; then the pipelined one, forced
+    # d = 128: the ping-pong kernel; then the pipelined one, forced
     assert lines[0].startswith("flash_attn: fwd_pingpong<bf16, 128, causal, whole> grid "), lines
     assert lines[1].startswith("flash_attn: fwd_sp<bf16, 128, causal> grid 16 x 512, 16 items"), lines
     assert any("bwd_dkdv<bf16, 128, causal>" in l for l in lines[2:]), lines
