@@ -418,48 +418,54 @@ def _time_calls(step, steps, warmup, stream):
 
 
 def run_fp8(args):
-    """Diagnostic line: the FP8 forward at the headline shape (B2 H32 N4096 d128 causal)."""
+    """Diagnostic lines: the FP8 forward at the headline shape (B2 H32 N4096 d128 causal)
+    and at the same shape with d = 64, E4M3 and E5M2."""
     import torch
 
     import exact_attention_flash_amd as fa
     from exact_attention_flash_amd import inputs
 
-    w = inputs.WORKLOADS[inputs.HEADLINE]
+    head = inputs.WORKLOADS[inputs.HEADLINE]
+    d64 = inputs.Workload("llama7b_shape_b2_h32_n4096_d64_causal", head.B, head.H, head.N, 64, head.dtype,
+                          head.sigma, (True,), head.seed)
     dev = torch.device("cuda:0")
-    qb, kb, vb = inputs.workload_qkv(w)
-    q, k, v = (inputs.to_torch(x, w.dtype, dev) for x in (qb, kb, vb))
     stream = torch.cuda.current_stream(dev)
-    scale = inputs.default_scale(w.d)
-    for fmt in ("e4m3", "e5m2"):
-        q8, qs = fa.quantize_fp8(q, fmt=fmt)
-        k8, ks = fa.quantize_fp8(k, fmt=fmt)
-        v8, vs = fa.quantize_fp8(v, keys_transposed=True, fmt=fmt)
-        o = torch.empty_like(q)
-        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    for w in (head, d64):
+        qb, kb, vb = inputs.workload_qkv(w)
+        q, k, v = (inputs.to_torch(x, w.dtype, dev) for x in (qb, kb, vb))
+        scale = inputs.default_scale(w.d)
+        for fmt in ("e4m3", "e5m2"):
+            q8, qs = fa.quantize_fp8(q, fmt=fmt)
+            k8, ks = fa.quantize_fp8(k, fmt=fmt)
+            v8, vs = fa.quantize_fp8(v, keys_transposed=True, fmt=fmt)
+            o = torch.empty_like(q)
+            lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
 
-        def attn():
-            fa.flash_attn_fwd_fp8(q8, k8, v8, qs, ks, vs, o, lse, causal=True, scale=scale, stream=stream, fmt=fmt)
+            def attn():
+                fa.flash_attn_fwd_fp8(q8, k8, v8, qs, ks, vs, o, lse, causal=True, scale=scale, stream=stream,
+                                      fmt=fmt)
 
-        def quant():
-            fa.quantize_fp8(q, stream=stream, fmt=fmt)
-            fa.quantize_fp8(k, stream=stream, fmt=fmt)
-            fa.quantize_fp8(v, keys_transposed=True, stream=stream, fmt=fmt)
+            def quant():
+                fa.quantize_fp8(q, stream=stream, fmt=fmt)
+                fa.quantize_fp8(k, stream=stream, fmt=fmt)
+                fa.quantize_fp8(v, keys_transposed=True, stream=stream, fmt=fmt)
 
-        ms, med = _time_calls(attn, args.steps, args.warmup, stream)
-        qms, _ = _time_calls(quant, max(10, args.steps // 4), args.warmup, stream)
-        flops = w.flops(True)
-        tf = flops / (ms * 1e-3) / 1e12
-        in_bytes = 3 * w.B * w.H * w.N * w.d * 2
-        print(json.dumps({
-            "metric": "attention fwd TFLOP/s on FP8 inputs (diagnostic)",
-            "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": True,
-                       "inputs": f"{fmt.upper()}, power-of-two scale per 64 rows", "out_dtype": w.dtype},
-            "value": round(tf, 2), "unit": "TFLOP/s", "launch_ms": round(ms, 5), "launch_ms_median": round(med, 5),
-            "pct_of_fp8_peak": round(100 * tf / PEAK_FP8_TFLOPS, 2),
-            "pct_of_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
-            "quantize_q_k_v_ms": round(qms, 5),
-            "quantize_GB_per_s": round((in_bytes + in_bytes / 2) / (qms * 1e-3) / 1e9, 1),
-            "steps": args.steps, "warmup": args.warmup}), flush=True)
+            ms, med = _time_calls(attn, args.steps, args.warmup, stream)
+            qms, _ = _time_calls(quant, max(10, args.steps // 4), args.warmup, stream)
+            flops = w.flops(True)
+            tf = flops / (ms * 1e-3) / 1e12
+            in_bytes = 3 * w.B * w.H * w.N * w.d * 2
+            print(json.dumps({
+                "metric": "attention fwd TFLOP/s on FP8 inputs (diagnostic)",
+                "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": True,
+                           "inputs": f"{fmt.upper()}, power-of-two scale per 64 rows", "out_dtype": w.dtype},
+                "value": round(tf, 2), "unit": "TFLOP/s", "launch_ms": round(ms, 5),
+                "launch_ms_median": round(med, 5),
+                "pct_of_fp8_peak": round(100 * tf / PEAK_FP8_TFLOPS, 2),
+                "pct_of_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+                "quantize_q_k_v_ms": round(qms, 5),
+                "quantize_GB_per_s": round((in_bytes + in_bytes / 2) / (qms * 1e-3) / 1e9, 1),
+                "steps": args.steps, "warmup": args.warmup}), flush=True)
 
 
 def run(args, workload_name, causal):

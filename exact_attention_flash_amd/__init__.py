@@ -321,7 +321,7 @@ def quantize_fp8(x, keys_transposed: bool = False, stream=None, fmt: str = "e4m3
 def flash_attn_fwd_fp8(q8, k8, v8t, q_scale, k_scale, v_scale, o, lse, causal: bool = False,
                        scale: float | None = None, stream=None, fmt: str = "e4m3") -> None:
     """The FP8 forward on caller-owned tensors (outputs of quantize_fp8 in format fmt;
-    o [B, H, N, 128] bf16/fp16 and lse [B, H, N] float32)."""
+    o [B, H, N, d] bf16/fp16 with d 64 or 128, and lse [B, H, N] float32)."""
     import torch
 
     B, H, N, d = o.shape

@@ -475,7 +475,7 @@ int check_fp8(const void* q8, const void* k8, const void* v8t, const int32_t* qs
               float scale, int out_dtype, int format, fa::Fp8Args* a, bool* empty) {
   *empty = false;
   if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
-  if (d != 128) return FA_ERR_HEADDIM;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
   if (out_dtype != FA_BF16 && out_dtype != FA_FP16) return FA_ERR_DTYPE;
   if (causal != 0 && causal != 1) return FA_ERR_ARG;
   if (format != FA_FP8_E4M3 && format != FA_FP8_E5M2) return FA_ERR_ARG;
@@ -557,8 +557,8 @@ extern "C" int flash_attn_fwd_fp8(const void* q8, const void* k8, const void* v8
   const int st = check_fp8(q8, k8, v8t, q_scale, k_scale, v_scale, o, lse, B, H, N, d, causal, scale, out_dtype,
                            format, &a, &empty);
   if (st != FA_OK || empty) return st;
-  const hipError_t err = fa::launch_fwd_fp8(a, out_dtype == FA_FP16, causal == 1, format == FA_FP8_E5M2,
-                                            static_cast<hipStream_t>(stream));
+  const hipError_t err = fa::launch_fwd_fp8(a, static_cast<int>(d), out_dtype == FA_FP16, causal == 1,
+                                            format == FA_FP8_E5M2, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

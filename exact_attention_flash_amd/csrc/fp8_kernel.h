@@ -18,15 +18,15 @@ struct QuantArgs {
   int t64;          // ceil(n / 64)
 };
 
-// Attention forward on quantized inputs (d = 128).
+// Attention forward on quantized inputs (d = 64 or 128).
 struct Fp8Args {
-  const uint8_t* q8;     // [bh, n, 128] FP8 (E4M3 or E5M2)
-  const uint8_t* k8;     // [bh, n, 128] FP8
-  const uint8_t* v8t;    // [bh, t64, 128, 64] FP8, keys-transposed layout
+  const uint8_t* q8;     // [bh, n, d] FP8 (E4M3 or E5M2)
+  const uint8_t* k8;     // [bh, n, d] FP8
+  const uint8_t* v8t;    // [bh, t64, d, 64] FP8, keys-transposed layout
   const int32_t* q_se;   // [bh, t64] E8M0 codes of the blocks' scales
   const int32_t* k_se;
   const int32_t* v_se;
-  void* o;               // [bh, n, 128] bf16 or fp16
+  void* o;               // [bh, n, d] bf16 or fp16
   float* lse;            // [bh, n]
   int bh;
   int n;
@@ -38,9 +38,9 @@ struct Fp8Args {
                          // instruction does not take it as a literal)
 };
 
-// Enqueue the FP8 forward; sizes the persistent grid from the device's compute units.
-// e5m2: q8, k8 and v8t hold E5M2 codes (else E4M3).
-hipError_t launch_fwd_fp8(const Fp8Args& a, bool fp16_out, bool causal, bool e5m2, hipStream_t stream);
+// Enqueue the FP8 forward for head dimension d (64 or 128); sizes the persistent grid
+// from the device's compute units. e5m2: q8, k8 and v8t hold E5M2 codes (else E4M3).
+hipError_t launch_fwd_fp8(const Fp8Args& a, int d, bool fp16_out, bool causal, bool e5m2, hipStream_t stream);
 
 // Keys-transposed layout: position p (0..63) of a block row holds key
 // 32 * ((p % 32) / 16) + 8 * ((p % 16) / 4) + 4 * (p / 32) + p % 4 of the block.

@@ -1,4 +1,4 @@
-// Exact attention forward on FP8 (E4M3 or E5M2) inputs for gfx950, d = 128, bf16/fp16 out.
+// Exact attention forward on FP8 (E4M3 or E5M2) inputs for gfx950, d = 64 or 128, bf16/fp16 out.
 //
 // "FlashAttention: IO-Aware Tiling, Online Softmax Mathematics, Memory Hierarchy
 // Dynamics, and Kernel Evolution", section on FlashAttention-3: attention in 8-bit
@@ -15,7 +15,7 @@
 // instruction's operand scales,
 // so every score and every P V contribution is exact in scale:
 //  * S^T = K Q^T: A = 32 key rows of the K tile (LDS), B = the wave's 32 query
-//    rows (registers), two k-steps of 64 over d; scales = the K tile's and the Q
+//    rows (registers), d / 64 k-steps of 64 over d; scales = the K tile's and the Q
 //    block's exponents.
 //  * O^T += V^T P^T: A = 32 rows (head-dimension columns) of the V^T tile (LDS),
 //    B = P^T packed to E4M3 in registers from the S^T accumulator; the byte order
@@ -51,22 +51,34 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;   // query rows per item
 constexpr int kBN = kFp8Block;     // keys per tile = rows per quantization block
-constexpr int kD = 128;
 constexpr int kStages = 3;
 constexpr int kAhead = kStages - 2;
+constexpr int kScale = 256;  // one tile scale replicated by the 64 lanes of a load
 
-constexpr int kRow = kD;                    // bytes of a K or Q row
-constexpr int kTile = kBN * kRow;           // K tile bytes (= V^T tile bytes: 128 rows of 64)
-constexpr int kScale = 256;                 // one tile scale replicated by the 64 lanes of a load
-constexpr int kStage = 2 * kTile + 2 * kScale;
-constexpr int kQBytes = kBM * kRow;
-constexpr int kLoadsPerTile = 2 * (kTile / 1024) / kWaves + 2;  // K, V blocks + the two scales
-constexpr int kQLoads = kQBytes / 1024 / kWaves + 1;            // Q blocks + the Q scales
-
-// 16-byte chunk swizzles: rows of 8 chunks (K, Q) and of 4 chunks (V^T), so that
-// 16 consecutive rows read at one logical chunk hit every LDS bank once
+// 16-byte chunk swizzles: rows of 8 chunks (K and Q at d = 128) and of 4 chunks (K
+// and Q at d = 64, V^T), so that 16 consecutive rows read at one logical chunk hit
+// every LDS bank once
 __device__ __forceinline__ int swz8(int row) { return (((row >> 1) & 1) << 2) | ((row >> 2) & 3); }
 __device__ __forceinline__ int swz4(int row) { return (row >> 2) & 3; }
+
+// Sizes for head dimension D (64 or 128).
+template <int D>
+struct Geo8 {
+  static constexpr int kRow = D;                   // bytes of a K or Q row
+  static constexpr int kChunks = D / 16;           // 16-byte chunks of a K or Q row
+  static constexpr int kTile = kBN * kRow;         // K tile bytes (= V^T tile bytes: D rows of 64)
+  static constexpr int kStage = 2 * kTile + 2 * kScale;
+  static constexpr int kQBytes = kBM * kRow;
+  static constexpr int kBlocks = kTile / 1024;     // 1 KiB blocks of the K tile (and of the V^T tile)
+  // every wave loads one block of K and one of V^T (D = 128), or one block of either
+  // (D = 64: waves 0-3 K, waves 4-7 V^T)
+  static constexpr int kTileLoads = 2 * kBlocks / kWaves;
+  static constexpr int kQLoads = kQBytes / 1024 / kWaves + 1;  // Q blocks + the Q scales
+  static constexpr int kSteps = D / 32;            // products of S (and of P V) per tile
+  static_assert(D == 64 || D == 128, "FP8 instances: d = 64 or 128");
+  static_assert(kTileLoads == 1 || kTileLoads == 2, "whole 1 KiB blocks per wave");
+  __device__ static __forceinline__ int swz(int row) { return D == 128 ? swz8(row) : swz4(row); }
+};
 
 // FA (A operand) and FB (B operand) select the instruction's operand formats: 0 =
 // E4M3, 1 = E5M2
@@ -80,8 +92,10 @@ __device__ __forceinline__ int pack4(float a, float b, float c, float d) {
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false), true);
 }
 
-template <bool FP16OUT, bool CAUSAL, bool E5>
+template <bool FP16OUT, bool CAUSAL, bool E5, int kD>
 __global__ __launch_bounds__(kThreads, 1) void fwd_fp8(Fp8Args a) {
+  using G = Geo8<kD>;
+  constexpr int kRow = G::kRow, kTile = G::kTile, kStage = G::kStage, kQBytes = G::kQBytes;
   constexpr int kIn = E5 ? 1 : 0;  // format code of Q, K and V; P is always E4M3
   __shared__ __attribute__((aligned(1024))) char smem[kStages * kStage + kQBytes + kScale];
   char* const qsm = smem + kStages * kStage;
@@ -117,9 +131,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8(Fp8Args a) {
   auto item_tiles = [&](int q0) { return CAUSAL ? min(tiles_all, (min(q0 + kBM, N) - 1) / kBN + 1) : tiles_all; };
   const int wave_rows = 32 * (grp == 0 ? (wave & 3) : 7 - (wave & 3));
 
-  // DMA offsets: one 1 KiB block of the K tile and one of the V^T tile per wave
-  const int kp = 64 * wave + lane;
-  const uint32_t k_ld = (uint32_t)(kp / 8) * kRow + (uint32_t)(((kp % 8) ^ swz8(kp / 8)) * 16);
+  // DMA offsets: block blk of the K tile and of the V^T tile (D = 128: blk = wave,
+  // both tiles; D = 64: wave w < 4 loads K block w, wave w >= 4 V^T block w - 4)
+  const int blk = G::kTileLoads == 2 ? wave : (wave & 3);
+  // wave-uniform choice of the one tile a wave loads at D = 64 (a scalar branch)
+  const bool loads_k = __builtin_amdgcn_readfirstlane(wave) < 4;
+  const int kp = 64 * blk + lane;
+  const uint32_t k_ld = (uint32_t)(kp / G::kChunks) * kRow +
+                        (uint32_t)(((kp % G::kChunks) ^ G::swz(kp / G::kChunks)) * 16);
   const uint32_t v_ld = (uint32_t)(kp / 4) * kBN + (uint32_t)(((kp % 4) ^ swz4(kp / 4)) * 16);
 
   int c_r = 0, c_j = item_index(0), c_t = 0, c_n = 0, c_g = 0, c_bh = 0;
@@ -139,8 +158,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8(Fp8Args a) {
     const __amdgpu_buffer_rsrc_t ksr = buffer_rsrc(a.k_se + (int64_t)c_bh * T + c_t, 4u);
     const __amdgpu_buffer_rsrc_t vsr = buffer_rsrc(a.v_se + (int64_t)c_bh * T + c_t, 4u);
     char* st = smem + (c_g % kStages) * kStage;
-    buffer_load16_lds(kr, k_ld, st + 1024 * wave);
-    buffer_load16_lds(vr, v_ld, st + kTile + 1024 * wave);
+    if constexpr (G::kTileLoads == 2) {
+      buffer_load16_lds(kr, k_ld, st + 1024 * blk);
+      buffer_load16_lds(vr, v_ld, st + kTile + 1024 * blk);
+    } else if (loads_k) {
+      buffer_load16_lds(kr, k_ld, st + 1024 * blk);
+    } else {
+      buffer_load16_lds(vr, v_ld, st + kTile + 1024 * blk);
+    }
     buffer_load4_lds(ksr, 0u, st + 2 * kTile);
     buffer_load4_lds(vsr, 0u, st + 2 * kTile + kScale);
     ++c_g;
@@ -161,8 +186,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8(Fp8Args a) {
 #pragma unroll
     for (int i = 0; i < kQBytes / 1024 / kWaves; ++i) {
       const int p = lw + 64 * kWaves * i;
-      const int row = p / 8;
-      buffer_load16_lds(qr, (uint32_t)row * kRow + (uint32_t)(((p % 8) ^ swz8(row)) * 16),
+      const int row = p / G::kChunks;
+      buffer_load16_lds(qr, (uint32_t)row * kRow + (uint32_t)(((p % G::kChunks) ^ G::swz(row)) * 16),
                         qsm + 1024 * (wave + kWaves * i));
     }
     const int b0 = q0 / kBN;
@@ -176,8 +201,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8(Fp8Args a) {
     asm volatile("" : "+v"(row));
 #pragma unroll
     for (int kk = 0; kk < kD / 64; ++kk) {
-      const u32x4 lo = lds_read16(qsm + row * kRow + (((4 * kk + 2 * h) ^ swz8(row)) * 16));
-      const u32x4 hi = lds_read16(qsm + row * kRow + (((4 * kk + 2 * h + 1) ^ swz8(row)) * 16));
+      const u32x4 lo = lds_read16(qsm + row * kRow + (((4 * kk + 2 * h) ^ G::swz(row)) * 16));
+      const u32x4 hi = lds_read16(qsm + row * kRow + (((4 * kk + 2 * h + 1) ^ G::swz(row)) * 16));
       qreg[kk] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
     }
     q_sc = *reinterpret_cast<const int*>(qscale + 4 * (wave_rows / kBN));
@@ -199,7 +224,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8(Fp8Args a) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int row = 32 * b + l32;
-        k_off[b][kk][i] = row * kRow + (((4 * kk + 2 * h + i) ^ swz8(row)) * 16);
+        k_off[b][kk][i] = row * kRow + (((4 * kk + 2 * h + i) ^ G::swz(row)) * 16);
       }
   int v_off[2];
 #pragma unroll
@@ -216,8 +241,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8(Fp8Args a) {
   int row0 = 0, qrow = 0, n_tiles = 0, g0 = 0;
   auto active = [&](int t) { return row0 < N && (!CAUSAL || t * kBN <= row0 + 31); };
 
-  // matrix phase of tile i: S^T(i) (4 MFMAs) and u += P(i-1) V(i-1) (4 MFMAs),
-  // interleaved; operand reads one step ahead
+  // matrix phase of tile i: S^T(i) (D/32 MFMAs: key block st % 2, k-step st / 2) and
+  // u += P(i-1) V(i-1) (D/32 MFMAs: columns 32 st ..), interleaved; operand reads one
+  // step ahead
   auto mfma_steps = [&](auto do_s_c, auto do_p_c, int i) {
     constexpr bool DO_S = decltype(do_s_c)::value;
     constexpr bool DO_P = decltype(do_p_c)::value;
@@ -243,8 +269,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8(Fp8Args a) {
     };
     issue(0);
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      if (st + 1 < 4) issue(st + 1);
+    for (int st = 0; st < G::kSteps; ++st) {
+      if (st + 1 < G::kSteps) issue(st + 1);
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (DO_S) s[st & 1] = mfma8<kIn, kIn>(ka[st & 1][0], ka[st & 1][1], qreg[st >> 1], s[st & 1], ks, q_sc);
       if constexpr (DO_P) acc[st] = mfma8<kIn, 0>(va[st & 1][0], va[st & 1][1], pb, acc[st], vs, one);
@@ -335,7 +361,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8(Fp8Args a) {
         mfma_phase(i);
       }
       if (i + 1 < n_tiles) {
-        if (q_in_flight) wait_vmcnt<kQLoads>();
+        if (q_in_flight) wait_vmcnt<G::kQLoads>();
         else wait_vmcnt<0>();
         __syncthreads();
       }
@@ -365,20 +391,20 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8(Fp8Args a) {
 
 }  // namespace f8
 
-template <bool E5>
+template <bool E5, int D>
 hipError_t launch_fmt(const Fp8Args& a, int grid, bool fp16_out, bool causal, hipStream_t stream) {
   using namespace f8;
   if (fp16_out) {
-    if (causal) hipLaunchKernelGGL((fwd_fp8<true, true, E5>), dim3(grid), dim3(kThreads), 0, stream, a);
-    else hipLaunchKernelGGL((fwd_fp8<true, false, E5>), dim3(grid), dim3(kThreads), 0, stream, a);
+    if (causal) hipLaunchKernelGGL((fwd_fp8<true, true, E5, D>), dim3(grid), dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL((fwd_fp8<true, false, E5, D>), dim3(grid), dim3(kThreads), 0, stream, a);
   } else {
-    if (causal) hipLaunchKernelGGL((fwd_fp8<false, true, E5>), dim3(grid), dim3(kThreads), 0, stream, a);
-    else hipLaunchKernelGGL((fwd_fp8<false, false, E5>), dim3(grid), dim3(kThreads), 0, stream, a);
+    if (causal) hipLaunchKernelGGL((fwd_fp8<false, true, E5, D>), dim3(grid), dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL((fwd_fp8<false, false, E5, D>), dim3(grid), dim3(kThreads), 0, stream, a);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_fp8(const Fp8Args& args, bool fp16_out, bool causal, bool e5m2, hipStream_t stream) {
+hipError_t launch_fwd_fp8(const Fp8Args& args, int d, bool fp16_out, bool causal, bool e5m2, hipStream_t stream) {
   using namespace f8;
   Fp8Args a = args;
   const int cus = device_cus();
@@ -389,9 +415,13 @@ hipError_t launch_fwd_fp8(const Fp8Args& args, bool fp16_out, bool causal, bool 
     grid &= ~7;
     if (grid < 8) grid = 8;
   }
-  launch_log("fwd_fp8<%s out, %s, %s> grid %d x %d", dtype_name(fp16_out), causal ? "causal" : "full",
+  launch_log("fwd_fp8<%s out, %d, %s, %s> grid %d x %d", dtype_name(fp16_out), d, causal ? "causal" : "full",
              e5m2 ? "E5M2" : "E4M3", grid, kThreads);
-  return e5m2 ? launch_fmt<true>(a, grid, fp16_out, causal, stream) : launch_fmt<false>(a, grid, fp16_out, causal, stream);
+  if (d == 64)
+    return e5m2 ? launch_fmt<true, 64>(a, grid, fp16_out, causal, stream)
+                : launch_fmt<false, 64>(a, grid, fp16_out, causal, stream);
+  return e5m2 ? launch_fmt<true, 128>(a, grid, fp16_out, causal, stream)
+              : launch_fmt<false, 128>(a, grid, fp16_out, causal, stream);
 }
 
 }  // namespace fa

@@ -211,12 +211,12 @@ int flash_attn_quantize_fp8_validate(const void* x, void* x8, int32_t* scale_cod
  * rounded to E4M3 for the P V product (relative to the row maximum, times 2^8),
  * while the row sums use them unrounded.
  *
- * q8, k8  : device, [B, H, N, 128] FP8 codes from flash_attn_quantize_fp8 (FA_FP8_ROWS).
- * v8t     : device, [B, H, T, 128, 64] FP8 codes from flash_attn_quantize_fp8 (FA_FP8_KEYS_T).
+ * q8, k8  : device, [B, H, N, d] FP8 codes from flash_attn_quantize_fp8 (FA_FP8_ROWS).
+ * v8t     : device, [B, H, T, d, 64] FP8 codes from flash_attn_quantize_fp8 (FA_FP8_KEYS_T).
  * q_scale, k_scale, v_scale : device, [B, H, T] int32 scale codes of q8, k8, v8t.
- * o       : device, written, contiguous [B, H, N, 128] of out_dtype.
+ * o       : device, written, contiguous [B, H, N, d] of out_dtype.
  * lse     : device, written, contiguous [B, H, N] fp32.
- * d       : 128 (FA_ERR_HEADDIM otherwise). causal, scale, stream: as for flash_attn_fwd.
+ * d       : 64 or 128 (FA_ERR_HEADDIM otherwise). causal, scale, stream: as for flash_attn_fwd.
  * out_dtype : FA_BF16 or FA_FP16.
  * format  : FA_FP8_E4M3 or FA_FP8_E5M2, the format of q8, k8 and v8t (all three;
  *           else FA_ERR_ARG). P is rounded to E4M3 in either case.

@@ -443,7 +443,8 @@ def _fargs(q8=A, k8=A + GB, v8t=A + 2 * GB, qs=A + 3 * GB, ks=A + 3 * GB + 4096,
 
 
 BAD_FP8 = [
-    (dict(d=64), fa.FA_ERR_HEADDIM), (dict(dtype=2), fa.FA_ERR_DTYPE), (dict(causal=3), fa.FA_ERR_ARG),
+    (dict(d=96), fa.FA_ERR_HEADDIM), (dict(d=256), fa.FA_ERR_HEADDIM), (dict(dtype=2), fa.FA_ERR_DTYPE),
+    (dict(causal=3), fa.FA_ERR_ARG),
     (dict(fmt=7), fa.FA_ERR_ARG),
     (dict(scale=0.0), fa.FA_ERR_SCALE), (dict(B=-1), fa.FA_ERR_SHAPE),
     (dict(v8t=None), fa.FA_ERR_NULL), (dict(ks=None), fa.FA_ERR_NULL), (dict(lse=None), fa.FA_ERR_NULL),
@@ -463,6 +464,7 @@ def test_fp8_accepts_and_empty():
     assert _native.validate_fp8_raw(*_fargs()) == fa.FA_OK
     assert _native.validate_fp8_raw(*_fargs(causal=1, dtype=1)) == fa.FA_OK
     assert _native.validate_fp8_raw(*_fargs(fmt=fa.FA_FP8_E5M2)) == fa.FA_OK
+    assert _native.validate_fp8_raw(*_fargs(d=64)) == fa.FA_OK
     assert _native.fp8_raw(*_fargs(q8=None, k8=None, v8t=None, qs=None, ks=None, vs=None, o=None, lse=None,
                                    H=0)) == fa.FA_OK
 

@@ -142,7 +142,8 @@ def _fp8_case(fa, shape, dtype, causal, sigma, seed, heads=None, scale=None, fmt
     return worst, float(np.mean(means)), max(vs_orig), max(lse_max)
 
 
-SMALL = [(1, 1, 1, 128), (1, 2, 63, 128), (2, 1, 130, 128), (1, 2, 257, 128), (1, 1, 700, 128)]
+SMALL = [(1, 1, 1, 128), (1, 2, 63, 128), (2, 1, 130, 128), (1, 2, 257, 128), (1, 1, 700, 128),
+         (1, 1, 1, 64), (1, 2, 63, 64), (2, 1, 130, 64), (1, 2, 257, 64), (1, 1, 700, 64)]
 
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
@@ -156,8 +157,22 @@ def test_fp8_small(fa, shape, dtype, causal, fmt):
 
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp8_multi_item_workgroups(fa, d, causal, fmt):
+    """Several work items per workgroup (16 x 32 slices of two 256-row query tiles,
+    the last ragged: 1024 items on at most 256 workgroups), sampled heads."""
+    shape, dtype = (16, 32, 450, d), inputs.BF16
+    w, mean, orig, le = _fp8_case(fa, shape, dtype, causal, 1.0, 1300 + d + int(causal), heads=[0, 257, 511],
+                                  fmt=fmt)
+    _log(f"fp8 {fmt} multi-item {shape} causal={causal}: error/bound {w:.3f}, mean |err| {mean:.2e}, "
+         f"LSE err {le:.2e}, max |O - O(unquantized)| {orig:.2e}")
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
 @pytest.mark.parametrize("name,heads", [("llama7b_b2_h32_n4096_d128_causal", [0, 40, 63]),
-                                        ("stress_b3_h8_n4099_d128_sigma8", [0, 23])])
+                                        ("stress_b3_h8_n4099_d128_sigma8", [0, 23]),
+                                        ("mha_b4_h16_n1024_d64", [0, 37, 63])])
 def test_fp8_workloads(fa, name, heads, fmt):
     w = inputs.WORKLOADS[name]
     for causal in w.causal:
