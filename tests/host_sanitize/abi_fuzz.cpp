@@ -20,6 +20,7 @@
 namespace {
 int g_launches = 0;
 int g_kernel = 0;  // forward kernel of the last unsplit launch (FA_FWD_KERNEL_*)
+int g_fp8_d = 0;   // head dimension of the last FP8 launch
 fa::FwdArgs g_fwd;
 }  // namespace
 
@@ -48,7 +49,9 @@ hipError_t launch_quant_fp8(const QuantArgs&, bool, int, bool, bool, hipStream_t
   ++g_launches;
   return hipSuccess;
 }
-hipError_t launch_fwd_fp8(const Fp8Args&, bool, bool, bool, hipStream_t) {
+hipError_t launch_fwd_fp8(const Fp8Args&, int d, bool, bool, bool, hipStream_t) {
+  if (d != 64 && d != 128) std::abort();
+  g_fp8_d = d;
   ++g_launches;
   return hipSuccess;
 }
@@ -152,6 +155,12 @@ void known_cases() {
   CHECK(flash_attn_quantize_fp8(q, o, se, 1, 2, 100, 128, FA_FP8_KEYS_T, nullptr, FA_BF16, 3) == FA_ERR_ARG);
   CHECK(flash_attn_fwd_fp8(q, k, v, se, se + 64, se + 128, o, lse, 1, 2, 100, 128, 1, 0.1f, nullptr, FA_BF16,
                            FA_FP8_E4M3) == FA_OK);
+  CHECK(g_fp8_d == 128);
+  CHECK(flash_attn_fwd_fp8(q, k, v, se, se + 64, se + 128, o, lse, 1, 2, 100, 64, 0, 0.1f, nullptr, FA_FP16,
+                           FA_FP8_E5M2) == FA_OK);
+  CHECK(g_fp8_d == 64);
+  CHECK(flash_attn_fwd_fp8(q, k, v, se, se + 64, se + 128, o, lse, 1, 2, 100, 96, 0, 0.1f, nullptr, FA_FP16,
+                           FA_FP8_E5M2) == FA_ERR_HEADDIM);
   float* delta = reinterpret_cast<float*>(base + 8 * GB);
   CHECK(flash_attn_bwd(q, k, v, o, base + 5 * GB, lse, base + 9 * GB, base + 10 * GB, base + 11 * GB, delta, 2, 32,
                        4096, 128, 1, 0.088f, nullptr, FA_BF16) == FA_OK);
