@@ -208,6 +208,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
     k_ld[i] = live ? (uint32_t)row * (uint32_t)(2 * a.k_sn) + (uint32_t)(logical * 16) : kMaskedOffset;
     v_ld[i] = live ? (uint32_t)row * (uint32_t)(2 * a.v_sn) + (uint32_t)(logical * 16) : kMaskedOffset;
   }
+  // LDS byte address of this wave's first 1 KiB block relative to a region, in a
+  // scalar register: the load addresses (M0) are then formed by the scalar unit
+  const uint32_t lds_w = __builtin_amdgcn_readfirstlane(1024u * (uint32_t)wave);
   // The workgroup's key tiles form one stream over its items; tile g of the stream
   // lives in ring stage g % kStages. A cursor walks the stream kAhead tiles ahead
   // of the matrix work, so the first tiles of the next item are in flight while the
@@ -232,11 +235,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
     const uint32_t v0 = (uint32_t)c_t * (uint32_t)(kBN * 2 * a.v_sn);
     const __amdgpu_buffer_rsrc_t kr = uniform_rsrc(reinterpret_cast<const char*>(c_k) + k0, a.k_ext - k0);
     const __amdgpu_buffer_rsrc_t vr = uniform_rsrc(reinterpret_cast<const char*>(c_v) + v0, a.v_ext - v0);
-    char* st = smem + c_st;
+    const uint32_t st = (uint32_t)(uintptr_t)smem + (uint32_t)c_st + lds_w;
 #pragma unroll
     for (int i = 0; i < G::blocksPerTile / kWaves; ++i) {
-      buffer_load16_lds(kr, k_ld[i], st + 1024 * (wave + kWaves * i));
-      buffer_load16_lds(vr, v_ld[i], st + G::tileBytes + 1024 * (wave + kWaves * i));
+      buffer_load16_lds_s(kr, k_ld[i], st + 1024 * kWaves * i);
+      buffer_load16_lds_s(vr, v_ld[i], st + G::tileBytes + 1024 * kWaves * i);
     }
     c_st = c_st + G::stageBytes == kStages * G::stageBytes ? 0 : c_st + G::stageBytes;
     if (++c_t == c_n) {
@@ -269,7 +272,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
       const uint32_t off = logical * 8 < d_real
                                ? (uint32_t)row * (uint32_t)(2 * q_sn) + (uint32_t)(logical * 16)
                                : kMaskedOffset;
-      buffer_load16_lds(qr, off, qsm + 1024 * (wave + kWaves * i));
+      buffer_load16_lds_s(qr, off, (uint32_t)(uintptr_t)qsm + lds_w + 1024 * kWaves * i);
     }
   };
   u32x4 qreg[D / 16];

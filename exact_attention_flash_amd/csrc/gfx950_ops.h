@@ -110,6 +110,15 @@ __device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, uint
   asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(m0) : "memory");
 }
 
+// The same load with the LDS byte address given as a wave-uniform 32-bit value that
+// the scalar unit computed (the caller keeps its parts in scalar registers). A load
+// to LDS may follow a scalar write of M0 after one wait state (s_nop 0); neither the
+// descriptor nor M0 may have been written by a VALU instruction within five wait
+// states, which the build audit checks on the generated code.
+__device__ __forceinline__ void buffer_load16_lds_s(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t lds_addr) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(lds_addr) : "memory");
+}
+
 // 4 bytes per lane from the buffer straight into LDS at lds_base + 4 * lane
 // (buffer_load_dword ... lds); completion awaited with wait_vmcnt like the 16-byte form.
 __device__ __forceinline__ void buffer_load4_lds(__amdgpu_buffer_rsrc_t r, uint32_t off, char* lds_base) {

@@ -82,7 +82,8 @@ def test_dkdv_product_blocks_have_no_moves_or_spills():
 # themselves. The checks below walk the generated code in program order inside
 # each basic block, counting one wait state per instruction and k + 1 for s_nop k.
 
-_REG = re.compile(r"\b([vas])\[(\d+):(\d+)\]|\b([vas])(\d+)\b")
+_REG = re.compile(r"\b([vas])\[(\d+):(\d+)\]|\b([vas])(\d+)\b|\b(m0)\b")
+_M0 = ("m", 0)
 
 
 def _regs(text: str):
@@ -90,6 +91,8 @@ def _regs(text: str):
     for m in _REG.finditer(text):
         if m.group(1):
             out |= {(m.group(1), r) for r in range(int(m.group(2)), int(m.group(3)) + 1)}
+        elif m.group(6):
+            out.add(_M0)
         else:
             out.add((m.group(4), int(m.group(5))))
     return out
@@ -194,10 +197,15 @@ def _hazards(asm: str, kernel: str):
             op = ins.split()[0]
             ops = _operands(ins)
             if op.startswith("buffer_load") and ins.endswith("lds"):
-                reads = _regs(",".join(ops[1:]))
+                # the descriptor and soffset, and M0 (the LDS address, an implicit operand)
+                reads = _regs(",".join(ops[1:])) | {_M0}
                 for prev, w in _window(cfg, b, n, 5, True):
-                    if _is_valu(prev.split()[0]) and _regs(_operands(prev)[0]) & reads:
+                    pop = prev.split()[0]
+                    written = _regs(_operands(prev)[0]) if _operands(prev) else set()
+                    if _is_valu(pop) and written & reads:
                         bad.append(f"{kernel}: '{prev}' then '{ins}' within {w} wait states")
+                    elif pop.startswith("s_") and _M0 in written and w < 1:
+                        bad.append(f"{kernel}: '{prev}' then '{ins}' with no wait state after the M0 write")
             elif "mfma" in op:
                 srcs = _regs(",".join(ops[1:3]))
                 for prev, w in _window(cfg, b, n, 2, True):
@@ -226,6 +234,14 @@ def test_hazard_windows_follow_control_flow():
     loop = "\n".join(["_k:", "s_nop 7", ".LBB0_1:", "buffer_load_dwordx4 v2, s[4:7], 0 offen lds",
                        "v_readfirstlane_b32 s4, v1", "s_cbranch_scc1 .LBB0_1", "s_endpgm", ".Lfunc_end0:"])
     assert any("v_readfirstlane_b32 s4" in x for x in _hazards(loop, "_k"))
+    # M0 is read by every load to LDS: five wait states after a VALU write, one after a scalar one
+    m0 = ["_k:", "s_nop 7", "s_mov_b32 m0, s9", "buffer_load_dwordx4 v2, s[4:7], 0 offen lds", "s_endpgm",
+          ".Lfunc_end0:"]
+    assert any("s_mov_b32 m0" in x for x in _hazards("\n".join(m0), "_k"))
+    assert not _hazards("\n".join(m0[:3] + ["s_nop 0"] + m0[3:]), "_k")
+    m0v = ["_k:", "s_nop 7", "v_readfirstlane_b32 m0, v3", "s_nop 3", "buffer_load_dwordx4 v2, s[4:7], 0 offen lds",
+           "s_endpgm", ".Lfunc_end0:"]
+    assert any("v_readfirstlane_b32 m0" in x for x in _hazards("\n".join(m0v), "_k"))
 
 
 def test_uniform_addresses_are_not_sign_extended():
