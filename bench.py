@@ -21,9 +21,10 @@ dO), counted as 2.5x the forward's FLOPs (five N x N x d products instead of
 two), with the float64 backward oracle as its CPU baseline. --splitkv times the
 forward with and without the key split (flash_attn_fwd_splitkv, split count
 planned for this GPU) on the shapes that underfill it. --strided times
-flash_attn_fwd_strided at the headline shape with head dimensions 80 and 96 and
-with q, k, v taken from one packed [B, N, 3, H, d] tensor (FLOPs counted with the
-real d). --fp8 times the FP8 path at the headline shape: flash_attn_fwd_fp8 alone
+flash_attn_fwd_strided at the headline shape with head dimensions 80, 96, 192 and
+256 (the last two on the 256-wide instance, one launch per 128 columns of V and O)
+and with q, k, v taken from one packed [B, N, 3, H, d] tensor (FLOPs counted with
+the real d). --fp8 times the FP8 path at the headline shape: flash_attn_fwd_fp8 alone
 (the attention on quantized inputs, E4M3 and E5M2; FLOPs as the metric counts them,
 against the 5 PFLOP/s dense FP8 peak) and the three quantization calls. --table prints one
 line per workload and mask: launch-time median, p10 and p90, TFLOP/s, % of peak,
@@ -351,7 +352,8 @@ def run_strided(args):
     dev = torch.device("cuda:0")
     B, H, N = 2, 32, 4096
     cases = [("contiguous d=128 (plain entry)", 128, False), ("contiguous d=80", 80, False),
-             ("contiguous d=96", 96, False), ("packed qkv [B,N,3,H,d] d=128, o [B,N,H,d]", 128, True)]
+             ("contiguous d=96", 96, False), ("packed qkv [B,N,3,H,d] d=128, o [B,N,H,d]", 128, True),
+             ("contiguous d=256 (plain entry, two launches)", 256, False), ("contiguous d=192", 192, False)]
     for label, d, packed in cases:
         qb, kb, vb = inputs.draw_qkv((B, H, N, d), inputs.BF16, 1.0, 3)
         q0, k0, v0 = (inputs.to_torch(x, inputs.BF16, dev) for x in (qb, kb, vb))
@@ -365,7 +367,7 @@ def run_strided(args):
         lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
         scale = inputs.default_scale(d)
         stream = torch.cuda.current_stream(dev)
-        if d == 128 and not packed:
+        if d in (128, 256) and not packed:
             step = lambda: fa.flash_attn_fwd(q, k, v, o, lse, causal=True, scale=scale, stream=stream)
         else:
             step = lambda: fa.flash_attn_fwd_strided(q, k, v, o, lse, causal=True, scale=scale, stream=stream)

@@ -76,7 +76,7 @@ def flash_attn_fwd(q, k, v, o, lse, causal: bool = False, scale: float | None = 
 def flash_attn_fwd_strided(q, k, v, o, lse, causal: bool = False, scale: float | None = None,
                            stream=None) -> None:
     """The strided entry point on caller-owned [B, H, N, d] views (any strides with the
-    head dimension contiguous; d a multiple of 8 up to 128); lse [B, H, N] float32 with
+    head dimension contiguous; d a multiple of 8 up to 256); lse [B, H, N] float32 with
     contiguous rows."""
     import torch
 
@@ -109,14 +109,14 @@ def flash_attn_fwd_strided(q, k, v, o, lse, causal: bool = False, scale: float |
 
 def forward(q, k, v, causal: bool = False, scale: float | None = None, stream=None):
     """Allocate O (q's dtype, contiguous) and LSE (float32) and run the forward pass.
-    Returns (o, lse). Contiguous inputs with d of 64 or 128 take flash_attn_fwd; other
+    Returns (o, lse). Contiguous inputs with d of 64, 128 or 256 take flash_attn_fwd; other
     layouts and head dimensions take flash_attn_fwd_strided."""
     import torch
 
     B, H, N, d = q.shape
     o = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if d in (64, 128) and all(t.is_contiguous() for t in (q, k, v)):
+    if d in (64, 128, 256) and all(t.is_contiguous() for t in (q, k, v)):
         flash_attn_fwd(q, k, v, o, lse, causal=causal, scale=scale, stream=stream)
     else:
         flash_attn_fwd_strided(q, k, v, o, lse, causal=causal, scale=scale, stream=stream)

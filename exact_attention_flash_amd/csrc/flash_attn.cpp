@@ -38,31 +38,34 @@ bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p
 // instance). inst is the smallest instance width (64, 80, 96 or 128) that holds the
 // real head dimension.
 int pick_unsplit(int inst) {
+  if (inst > 128) return FA_FWD_KERNEL_PINGPONG;  // the wide instance exists only there
   const char* e = std::getenv("FLASH_ATTN_FWD_KERNEL");
   if (e != nullptr && std::strcmp(e, "pingpong") == 0) return FA_FWD_KERNEL_PINGPONG;
   if (e != nullptr && std::strcmp(e, "pipelined") == 0) return FA_FWD_KERNEL_PIPELINED;
   return inst == 64 || inst == 128 ? FA_FWD_KERNEL_PINGPONG : FA_FWD_KERNEL_PIPELINED;
 }
 
-int instance_width(int64_t d) { return d <= 64 ? 64 : d <= 80 ? 80 : d <= 96 ? 96 : 128; }
+int instance_width(int64_t d) { return d <= 64 ? 64 : d <= 80 ? 80 : d <= 96 ? 96 : d <= 128 ? 128 : 256; }
 
 // Calls with a key split always use the ping-pong kernel's split instance.
 hipError_t launch_unsplit(const fa::FwdArgs& a, bool fp16, int inst, bool causal, hipStream_t stream) {
   return pick_unsplit(inst) == FA_FWD_KERNEL_PIPELINED
              ? fa::launch_fwd_sp(a, fp16, inst, causal, stream)
-             : fa::launch_fwd(a, fp16, inst <= 64 ? 64 : 128, causal, stream);
+             : fa::launch_fwd(a, fp16, inst <= 64 ? 64 : inst <= 128 ? 128 : 256, causal, stream);
 }
 
 }  // namespace
 
-extern "C" int flash_attn_abi_version(void) { return 8; }
+extern "C" int flash_attn_abi_version(void) { return 9; }
 
 extern "C" const char* flash_attn_strerror(int status) {
   switch (status) {
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "B, H or N is negative or too large for the kernel's indexing";
-    case FA_ERR_HEADDIM: return "head dimension d must be 64 or 128";
+    case FA_ERR_HEADDIM:
+      return "head dimension d must be 64, 128 or 256 (strided calls: a multiple of 8 up to 256; key split and "
+             "FP8 calls: 64 or 128)";
     case FA_ERR_DTYPE: return "dtype must be FA_BF16 or FA_FP16";
     case FA_ERR_SCALE: return "scale must be finite and > 0";
     case FA_ERR_ALIGN: return "16-bit tensors must be 16-byte aligned and fp32 ones 4-byte aligned";
@@ -85,7 +88,7 @@ int check_args(const void* q, const void* k, const void* v, void* o, float* lse,
                int64_t N, int64_t d, int causal, float scale, int dtype, fa::FwdArgs* a, bool* empty) {
   *empty = false;
   if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
-  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (d != 64 && d != 128 && d != 256) return FA_ERR_HEADDIM;
   if (dtype != FA_BF16 && dtype != FA_FP16) return FA_ERR_DTYPE;
   if (causal != 0 && causal != 1) return FA_ERR_ARG;
   if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
@@ -131,6 +134,7 @@ int check_args(const void* q, const void* k, const void* v, void* o, float* lse,
   // contiguous [B, H, N, d] layout
   a->heads = static_cast<int>(H);
   a->d_real = static_cast<int>(d);
+  a->v_col0 = 0;
   a->q_sb = a->k_sb = a->v_sb = a->o_sb = H * N * d;
   a->q_sh = a->k_sh = a->v_sh = a->o_sh = N * d;
   a->q_sn = a->k_sn = a->v_sn = a->o_sn = static_cast<int>(d);
@@ -173,7 +177,7 @@ int check_strided(const void* q, const void* k, const void* v, void* o, float* l
                   const int64_t* ls, int causal, float scale, int dtype, fa::FwdArgs* a, bool* empty) {
   *empty = false;
   if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
-  if (d < 8 || d > 128 || d % 8 != 0) return FA_ERR_HEADDIM;
+  if (d < 8 || d > 256 || d % 8 != 0) return FA_ERR_HEADDIM;
   if (dtype != FA_BF16 && dtype != FA_FP16) return FA_ERR_DTYPE;
   if (causal != 0 && causal != 1) return FA_ERR_ARG;
   if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
@@ -237,6 +241,7 @@ int check_strided(const void* q, const void* k, const void* v, void* o, float* l
   a->part_lse = nullptr;
   a->heads = static_cast<int>(H);
   a->d_real = static_cast<int>(d);
+  a->v_col0 = 0;
   a->q_sb = qs[0]; a->q_sh = qs[1]; a->q_sn = static_cast<int>(qs[2]);
   a->k_sb = ks[0]; a->k_sh = ks[1]; a->k_sn = static_cast<int>(ks[2]);
   a->v_sb = vs[0]; a->v_sh = vs[1]; a->v_sn = static_cast<int>(vs[2]);
@@ -361,7 +366,7 @@ extern "C" int flash_attn_fwd_strided(const void* q, const void* k, const void* 
 
 extern "C" int flash_attn_fwd_kernel(int64_t N, int64_t d, int causal) {
   if (N < 0) return FA_ERR_SHAPE;
-  if (d < 8 || d > 128 || d % 8 != 0) return FA_ERR_HEADDIM;
+  if (d < 8 || d > 256 || d % 8 != 0) return FA_ERR_HEADDIM;
   if (causal != 0 && causal != 1) return FA_ERR_ARG;
   return pick_unsplit(instance_width(d));
 }
@@ -396,6 +401,7 @@ int splitkv_common(const void* q, const void* k, const void* v, void* o, float* 
                    int64_t N, int64_t d, int causal, float scale, int num_splits, void* workspace,
                    uint64_t workspace_bytes, int dtype, bool plan_on_device, fa::FwdArgs* a, bool* empty) {
   if (num_splits < 0) return FA_ERR_ARG;
+  if (d > 128) return FA_ERR_HEADDIM;  // the key split has instances for d = 64 and 128
   const int st = check_args(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, a, empty);
   if (st != FA_OK || *empty) return st;
   int splits = num_splits;

@@ -31,6 +31,9 @@ struct FwdArgs {
   // element to the end of its last row, ((n - 1) * row stride + d_real) * 2.
   int heads;
   int d_real;
+  // first column of V and O that a launch covers: 0, or 128 for the second launch
+  // of the wide (256) instance of the ping-pong kernel
+  int v_col0;
   int64_t q_sb, q_sh, k_sb, k_sh, v_sb, v_sh, o_sb, o_sh, l_sb, l_sh;
   int q_sn, k_sn, v_sn, o_sn;
   uint32_t q_ext, k_ext, v_ext;

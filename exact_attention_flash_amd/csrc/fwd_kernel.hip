@@ -98,17 +98,32 @@ constexpr float kBig = 0x1p15f;
 // host keeps slice extents below 2^31 bytes), so the load writes zeros to LDS
 constexpr uint32_t kMaskedOffset = 0x80000000u;
 
+// Instance width D: the head dimension of Q and K (the scores). D = 64 and 128 cover
+// V and O whole; the wide instance D = 256 covers one 128-column half of V and O per
+// launch (the host launches it once per half, each launch recomputing the scores),
+// and takes Q straight into registers, since a Q region of 256 wide rows would not
+// fit in LDS beside the ring.
 template <int D>
 struct Geo {
-  static constexpr int rowBytes = D * 2;
-  static constexpr int chunksPerRow = D / 8;  // 16-byte chunks
-  static constexpr int tileBytes = kBN * rowBytes;
-  static constexpr int stageBytes = 2 * tileBytes;  // K then V
-  static constexpr int qBytes = kBM * rowBytes;       // the Q rows of one item
-  static constexpr int blocksPerTile = tileBytes / 1024;  // 1 KiB per wave-instruction
-  static constexpr int qLoadsPerWave = qBytes / 1024 / kWaves;       // Q instructions per wave per item
-  static_assert(blocksPerTile % kWaves == 0, "tile must split into whole 1 KiB blocks per wave");
-  __device__ static __forceinline__ int swz(int row) { return chunk_swizzle<D>(row); }
+  static constexpr bool wide = D > 128;
+  static constexpr int DV = wide ? 128 : D;             // columns of V and O per launch
+  static constexpr int rowBytes = D * 2;                // a K (and Q) row
+  static constexpr int chunksPerRow = D / 8;            // 16-byte chunks of a K row
+  static constexpr int vRowBytes = DV * 2;              // a V row (its half, for the wide instance)
+  static constexpr int vChunksPerRow = DV / 8;
+  static constexpr int tileBytes = kBN * rowBytes;      // K tile
+  static constexpr int vTileBytes = kBN * vRowBytes;    // V tile
+  static constexpr int stageBytes = tileBytes + vTileBytes;  // K then V
+  static constexpr int qBytes = wide ? 0 : kBM * rowBytes;   // the Q rows of one item (LDS)
+  static constexpr int blocksPerTile = tileBytes / 1024;     // 1 KiB per wave-instruction
+  static constexpr int vBlocksPerTile = vTileBytes / 1024;
+  static constexpr int qLoadsPerWave = qBytes / 1024 / kWaves;  // Q instructions per wave per item
+  static_assert(blocksPerTile % kWaves == 0 && vBlocksPerTile % kWaves == 0,
+                "tile must split into whole 1 KiB blocks per wave");
+  // The XOR swizzle of a 16-byte chunk acts on the low four bits of its index; a
+  // 256-wide K row is two 128-wide halves with the same pattern.
+  __device__ static __forceinline__ int swz(int row) { return chunk_swizzle<(D > 128 ? 128 : D)>(row); }
+  __device__ static __forceinline__ int vswz(int row) { return chunk_swizzle<DV>(row); }
 };
 
 // The kernel's argument block, read from the kernel-argument segment where a field
@@ -199,14 +214,21 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
   // ---- direct-to-LDS tile loads: this wave fills blocks wave + 8*i of K and of V ----
   // lane `lane` of block b lands at chunk position 64*b + lane = (row, physical chunk);
   // it fetches the logical chunk physical ^ swz(row) of that row.
-  uint32_t k_ld[G::blocksPerTile / kWaves], v_ld[G::blocksPerTile / kWaves];
+  // (V: of the launch's columns v_col0 .. v_col0 + DV - 1)
+  uint32_t k_ld[G::blocksPerTile / kWaves], v_ld[G::vBlocksPerTile / kWaves];
 #pragma unroll
   for (int i = 0; i < G::blocksPerTile / kWaves; ++i) {
     const int p = 64 * (wave + kWaves * i) + lane;
     const int row = p / G::chunksPerRow, logical = (p % G::chunksPerRow) ^ G::swz(row);
     const bool live = logical * 8 < a.d_real;
     k_ld[i] = live ? (uint32_t)row * (uint32_t)(2 * a.k_sn) + (uint32_t)(logical * 16) : kMaskedOffset;
-    v_ld[i] = live ? (uint32_t)row * (uint32_t)(2 * a.v_sn) + (uint32_t)(logical * 16) : kMaskedOffset;
+  }
+#pragma unroll
+  for (int i = 0; i < G::vBlocksPerTile / kWaves; ++i) {
+    const int p = 64 * (wave + kWaves * i) + lane;
+    const int row = p / G::vChunksPerRow, col = (G::wide ? a.v_col0 : 0) + 8 * ((p % G::vChunksPerRow) ^ G::vswz(row));
+    const bool live = col < a.d_real;
+    v_ld[i] = live ? (uint32_t)row * (uint32_t)(2 * a.v_sn) + (uint32_t)(col * 2) : kMaskedOffset;
   }
   // LDS byte address of this wave's first 1 KiB block relative to a region, in a
   // scalar register: the load addresses (M0) are then formed by the scalar unit
@@ -239,7 +261,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
 #pragma unroll
     for (int i = 0; i < G::blocksPerTile / kWaves; ++i) {
       buffer_load16_lds_s(kr, k_ld[i], st + 1024 * kWaves * i);
-      buffer_load16_lds_s(vr, v_ld[i], st + G::tileBytes + 1024 * kWaves * i);
+      if (i < G::vBlocksPerTile / kWaves)
+        buffer_load16_lds_s(vr, v_ld[i], st + G::tileBytes + 1024 * kWaves * i);
     }
     c_st = c_st + G::stageBytes == kStages * G::stageBytes ? 0 : c_st + G::stageBytes;
     if (++c_t == c_n) {
@@ -276,6 +299,24 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
     }
   };
   u32x4 qreg[D / 16];
+  // wide instance: the wave's Q rows straight from memory into the B operands (rows
+  // past N and columns past d read as zeros); issued while the previous item drains
+  auto load_q_regs = [&](int j) {
+    const int q0 = item_q0(j);
+    KArgs* ka = kargs();
+    const int q_sn = ka->q_sn;
+    const __amdgpu_buffer_rsrc_t qr =
+        uniform_rsrc(reinterpret_cast<const uint16_t*>(ka->q) + slice_off(item_bh(j), ka->q_sb, ka->q_sh) +
+                        (int64_t)q0 * q_sn,
+                    ka->q_ext - (uint32_t)((int64_t)q0 * q_sn * 2));
+    const int d_real = ka->d_real;
+    const uint32_t rowoff = (uint32_t)(wave_rows + l32) * (uint32_t)(2 * q_sn);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const int col = 16 * kk + 8 * h;
+      qreg[kk] = buffer_load16(qr, col < d_real ? rowoff + (uint32_t)(2 * col) : kMaskedOffset);
+    }
+  };
   auto read_q = [&]() {
     int row = wave_rows + l32;
     asm volatile("" : "+v"(row));  // recomputed per call rather than kept live
@@ -287,7 +328,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
   // prologue: the first item's Q and the first kAhead tiles of the stream (the
   // cursor may move past the first item while doing so)
   const int first_j = c_j;
-  issue_q(first_j);
+  if constexpr (G::wide) load_q_regs(first_j);
+  else issue_q(first_j);
 #pragma unroll
   for (int t = 0; t < kAhead; ++t) issue_next();
   bool first = true;
@@ -300,20 +342,20 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
   // 4*db + 2*((lane/16)%2) + (lane%4)/2, byte 8*(lane%2) inside the chunk
   const int vk = (lane & 15) >> 2;
   const int vrow_base = 4 * h + vk;
-  int v_lane[2][D / 32];
+  int v_lane[2][G::DV / 32];
 #pragma unroll
   for (int half = 0; half < 2; ++half)
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
+    for (int db = 0; db < G::DV / 32; ++db) {
       const int row = 8 * half + vrow_base;
       const int logical = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-      v_lane[half][db] = row * G::rowBytes + ((logical ^ G::swz(row)) * 16) + 8 * (lane & 1);
+      v_lane[half][db] = row * G::vRowBytes + ((logical ^ G::vswz(row)) * 16) + 8 * (lane & 1);
     }
 
   const float sc = a.scale_log2;
   float m_run;  // reference maximum (log2 units) of this lane's query
   float l_run;  // denominator over this half-wave's keys
-  f32x16 acc[D / 32];
+  f32x16 acc[G::DV / 32];
   f32x16 s[2] = {f32x16{}, f32x16{}};
   u32x4 pb[4] = {u32x4{}, u32x4{}, u32x4{}, u32x4{}};
 
@@ -326,21 +368,26 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
   auto active = [&](int t) { return row0 < N && (!CAUSAL || key_tile(t) * kBN <= row0 + 31); };
 
   // per-lane K offsets: row l32 (the second block of 32 keys adds 32 rows), logical
-  // chunk 2*kk + h
-  int k_off[D / 16];
+  // chunk 2*kk + h; in a 256-wide row, chunk 16 + c sits 256 bytes after chunk c
+  constexpr int kOffs = D / 16 < 8 ? D / 16 : 8;
+  int k_off[kOffs];
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) k_off[kk] = k_lane + (((2 * kk + h) ^ krow_sw) * 16);
+  for (int kk = 0; kk < kOffs; ++kk) k_off[kk] = k_lane + (((2 * kk + h) ^ krow_sw) * 16);
+  auto koff = [&](int kk) { return k_off[kk % kOffs] + (kk / kOffs) * 256; };
 
   // Matrix phase of tile i: S^T(i) = K_i Q^T (D/8 MFMAs) and u += P(i-1) V(i-1)
-  // (D/8 MFMAs), interleaved one for one. Operand reads from LDS are issued kLook
-  // steps ahead of their MFMA so that LDS latency hides behind matrix work; the
-  // scheduling fences keep the compiler from regrouping reads next to their uses.
+  // (DV/8 MFMAs), one P V product after every kRatio S products. Operand reads from
+  // LDS are issued kLook steps ahead of their MFMA so that LDS latency hides behind
+  // matrix work; the scheduling fences keep the compiler from regrouping reads next
+  // to their uses.
   constexpr int kSteps = D / 8;
+  constexpr int kRatio = D / G::DV;
 #ifdef FA_LOOKAHEAD
   constexpr int kLook = FA_LOOKAHEAD;
 #else
   // (measured: 4 at D = 64 is 5% faster than 3; at D = 128, 3 and 4 are within 1%)
-  constexpr int kLook = D == 64 ? 4 : 3;
+  // (the wide instance looks two steps ahead: three would spill)
+  constexpr int kLook = D == 64 ? 4 : D > 128 ? 2 : 3;
 #endif
   auto mfma_steps = [&](auto do_s_c, auto do_p_c, int i) {
     constexpr bool DO_S = decltype(do_s_c)::value;
@@ -350,11 +397,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
     u32x4 kop[kLook + 1];
     u32x2 vlo[kLook + 1], vhi[kLook + 1];
     auto issue = [&](int st) {
-      if constexpr (DO_S) kop[st % (kLook + 1)] = lds_read16(kt + k_off[st >> 1] + (st & 1) * 32 * G::rowBytes);
+      if constexpr (DO_S) kop[st % (kLook + 1)] = lds_read16(kt + koff(st >> 1) + (st & 1) * 32 * G::rowBytes);
       if constexpr (DO_P) {
-        const int t = st / (D / 32), db = st % (D / 32);
-        vlo[st % (kLook + 1)] = lds_read_tr16(vt + v_lane[0][db] + 16 * t * G::rowBytes);
-        vhi[st % (kLook + 1)] = lds_read_tr16(vt + v_lane[1][db] + 16 * t * G::rowBytes);
+        if (st % kRatio == 0) {
+          const int pst = st / kRatio, t = pst / (G::DV / 32), db = pst % (G::DV / 32);
+          vlo[pst % (kLook + 1)] = lds_read_tr16(vt + v_lane[0][db] + 16 * t * G::vRowBytes);
+          vhi[pst % (kLook + 1)] = lds_read_tr16(vt + v_lane[1][db] + 16 * t * G::vRowBytes);
+        }
       }
     };
     if constexpr (DO_S) {
@@ -369,9 +418,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (DO_S) s[st & 1] = mfma32<FP16>(kop[st % (kLook + 1)], qreg[st >> 1], s[st & 1]);
       if constexpr (DO_P) {
-        const int t = st / (D / 32), db = st % (D / 32);
-        const int slot = st % (kLook + 1);
-        acc[db] = mfma32<FP16>(u32x4{vlo[slot][0], vlo[slot][1], vhi[slot][0], vhi[slot][1]}, pb[t], acc[db]);
+        if (st % kRatio == 0) {
+          const int pst = st / kRatio, t = pst / (G::DV / 32), db = pst % (G::DV / 32);
+          const int slot = pst % (kLook + 1);
+          acc[db] = mfma32<FP16>(u32x4{vlo[slot][0], vlo[slot][1], vhi[slot][0], vhi[slot][1]}, pb[t], acc[db]);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -459,7 +510,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
     m_run = m_new;
     if (__any(alpha != 1.0f)) {
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
+      for (int db = 0; db < G::DV / 32; ++db) acc[db] *= alpha;
     }
   };
 
@@ -470,7 +521,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
     if (first) wait_vmcnt<0>();
     first = false;
     __syncthreads();
-    read_q();
+    if constexpr (!G::wide) read_q();
     const int bh = item_bh(it_j);
     row0 = item_q0(it_j) + wave_rows;
     qrow = row0 + l32;
@@ -484,7 +535,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
     m_run = -INFINITY;
     l_run = 0.f;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
+    for (int db = 0; db < G::DV / 32; ++db) acc[db] = f32x16{};
 
     // once every wave holds its Q rows (this barrier), the next item's Q may be
     // loaded; it is issued after the first tile load so that the wait for that tile
@@ -499,7 +550,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
       // hundreds of cycles. Group A issues at the top; group B issues after its
       // softmax, when the queue has drained (tile first, then the next item's Q, so
       // that the wait below can leave only Q in flight).
-      const bool q_in_flight = i == 0 && next_j >= 0;
+      const bool q_in_flight = !G::wide && i == 0 && next_j >= 0;
+      // wide instance: the next item's Q goes straight to registers in the last
+      // iteration, which has no score product left (its loads land by the epilogue)
+      if constexpr (G::wide)
+        if (i == n_tiles && next_j >= 0) load_q_regs(next_j);
       // A: matrix work of tile i, then its softmax; B: softmax of tile i-1, then
       // matrix work of tile i
       // (the raised issue priority of the matrix phase starts before the loads, so
@@ -511,7 +566,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
       if (grp != 0) softmax_phase(i - 1);
       __builtin_amdgcn_s_setprio(1);
       if (i < n_tiles) issue_next();
-      if (q_in_flight) issue_q(next_j);
+      if constexpr (!G::wide)
+        if (q_in_flight) issue_q(next_j);
       mfma_phase(i);
       if (grp == 0) softmax_phase(i);
       // tile i+1 must have landed (every wave waits for its own loads) before the
@@ -528,7 +584,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
     // here, before the stores, so that the next item need not wait for the stores
     wait_vmcnt<0>();
     const float l_tot = l_run + other_half(l_run);
-    if (SPLIT && qrow < N) {
+    if constexpr (SPLIT) {
+      static_assert(!G::wide, "no key split for the wide instance");
+      if (qrow < N) {
       // partial of this key range: u / l and m + ln l in fp32 (a row with no
       // visible key in the range has l = 0: O = 0, LSE = -inf)
       const int64_t prow = ((int64_t)item_split(it_j) * a.bh + bh) * N + qrow;
@@ -545,16 +603,16 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
                     acc[db][4 * g + 3] * inv};
       if (h == 0)
         ka->part_lse[prow] = live ? (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994530942f : -INFINITY;
-    }
-    if (!SPLIT) {
+      }
+    } else {
       // Rounded output in 16-byte pieces: a lane holds four columns of each group of
       // eight and the lane 32 away the other four of the same row, so one swap of
       // the two halves' words gives the lower half all eight columns of an even
       // group and the upper half all eight of the odd group after it.
       const float inv = 1.0f / l_tot;
-      u32x4 w[D / 16];
+      u32x4 w[G::DV / 16];
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+      for (int db = 0; db < G::DV / 32; ++db)
 #pragma unroll
         for (int g = 0; g < 4; g += 2) {
           const uint32_t e0 = pack2<FP16>(acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv);
@@ -567,19 +625,21 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pingpong(FwdArgs a) {
         }
       if (qrow < N) {
         KArgs* ka = kargs();
-        const int d_real = ka->d_real;
-        uint16_t* og =
-            reinterpret_cast<uint16_t*>(ka->o) + slice_off(bh, ka->o_sb, ka->o_sh) + (int64_t)qrow * ka->o_sn + 8 * h;
-        if (d_real == D) {
+        // columns v_col0 .. v_col0 + DV - 1 of which the first d_real - v_col0 exist
+        const int d_real = ka->d_real - (G::wide ? ka->v_col0 : 0);
+        uint16_t* og = reinterpret_cast<uint16_t*>(ka->o) + slice_off(bh, ka->o_sb, ka->o_sh) +
+                       (int64_t)qrow * ka->o_sn + (G::wide ? ka->v_col0 : 0) + 8 * h;
+        if (d_real >= G::DV) {
 #pragma unroll
-          for (int k = 0; k < D / 16; ++k) *reinterpret_cast<u32x4*>(og + 16 * k) = w[k];
+          for (int k = 0; k < G::DV / 16; ++k) *reinterpret_cast<u32x4*>(og + 16 * k) = w[k];
         } else {
           // d_real is a multiple of 8: each piece is wholly inside or outside
 #pragma unroll
-          for (int k = 0; k < D / 16; ++k)
+          for (int k = 0; k < G::DV / 16; ++k)
             if (16 * k + 8 * h < d_real) *reinterpret_cast<u32x4*>(og + 16 * k) = w[k];
         }
-        if (h == 0)
+        // (both launches of the wide instance form the same LSE; the first stores it)
+        if (h == 0 && (!G::wide || ka->v_col0 == 0))
           ka->lse[slice_off(bh, ka->l_sb, ka->l_sh) + qrow] =
               (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994530942f;
       }
@@ -622,10 +682,21 @@ __global__ __launch_bounds__(256) void merge_splits(FwdArgs a) {
 
 template <bool FP16, int D, bool CAUSAL>
 hipError_t launch_one(const FwdArgs& a, hipStream_t stream) {
-  launch_log("fwd_pingpong<%s, %d, %s, %s> grid %d x %d, %d splits, %s order", dtype_name(FP16), D,
-             CAUSAL ? "causal" : "full", a.splits > 1 ? "split" : "whole", a.grid, kThreads, a.splits,
-             a.slice_major ? "slice-major" : "rank-major");
-  if (a.splits > 1) {
+  launch_log("fwd_pingpong<%s, %d, %s, %s> grid %d x %d, %d splits, %s order, columns from %d", dtype_name(FP16),
+             D, CAUSAL ? "causal" : "full", a.splits > 1 ? "split" : "whole", a.grid, kThreads, a.splits,
+             a.slice_major ? "slice-major" : "rank-major", a.v_col0);
+  if constexpr (D > 128) {
+    // the wide instance: one launch per 128-column half of V and O (no key split)
+    if (a.splits > 1) return hipErrorInvalidValue;
+    for (int c0 = 0; c0 < a.d_real; c0 += 128) {
+      FwdArgs h = a;
+      h.v_col0 = c0;
+      hipLaunchKernelGGL((fwd_pingpong<FP16, D, CAUSAL, false>), dim3(a.grid), dim3(kThreads), 0, stream, h);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  } else if (a.splits > 1) {
     hipLaunchKernelGGL((fwd_pingpong<FP16, D, CAUSAL, true>), dim3(a.grid), dim3(kThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -684,9 +755,11 @@ hipError_t launch_fwd(const FwdArgs& args, bool fp16, int d, bool causal, hipStr
                                                 group_items % (2 * group_wgs) == 0));
   if (fp16) {
     if (d == 64) return causal ? launch_one<true, 64, true>(a, stream) : launch_one<true, 64, false>(a, stream);
+    if (d == 256) return causal ? launch_one<true, 256, true>(a, stream) : launch_one<true, 256, false>(a, stream);
     return causal ? launch_one<true, 128, true>(a, stream) : launch_one<true, 128, false>(a, stream);
   }
   if (d == 64) return causal ? launch_one<false, 64, true>(a, stream) : launch_one<false, 64, false>(a, stream);
+  if (d == 256) return causal ? launch_one<false, 256, true>(a, stream) : launch_one<false, 256, false>(a, stream);
   return causal ? launch_one<false, 128, true>(a, stream) : launch_one<false, 128, false>(a, stream);
 }
 

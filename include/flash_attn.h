@@ -47,7 +47,8 @@ typedef enum {
   FA_OK = 0,
   FA_ERR_NULL = -1,    /* a required pointer is NULL (with non-empty work)        */
   FA_ERR_SHAPE = -2,   /* B, H or N negative, or a size overflows the kernel's indexing */
-  FA_ERR_HEADDIM = -3, /* d is not 64 or 128                                      */
+  FA_ERR_HEADDIM = -3, /* d is not 64, 128 or 256 (strided: a multiple of 8 up to
+                          256; key split and FP8: 64 or 128)                     */
   FA_ERR_DTYPE = -4,   /* dtype is neither FA_BF16 nor FA_FP16                    */
   FA_ERR_SCALE = -5,   /* scale is not finite or not > 0                          */
   FA_ERR_ALIGN = -6,   /* a 16-bit tensor not 16-byte aligned, or an fp32 one not 4-byte aligned */
@@ -82,7 +83,9 @@ typedef enum {
  * B, H, N : batch, heads, sequence length (queries and keys share N). Any of them
  *           zero means there is nothing to do: FA_OK is returned and no pointer is
  *           touched. Requires N * d < 2^31 and B * H * ceil(N / 256) < 2^31.
- * d       : head dimension, 64 or 128.
+ * d       : head dimension, 64, 128 or 256. With d = 256 the kernel runs twice, once
+ *           per 128-column half of v and o; each run recomputes the scores, so the
+ *           matrix work is 1.5 times that of one pass.
  * causal  : 0 for full attention, 1 for causal (top-left aligned: query i sees
  *           keys 0..i).
  * scale   : multiplier of q.k, finite and > 0 (usually 1/sqrt(d)).
@@ -124,13 +127,14 @@ int flash_attn_fwd_validate(const void* q, const void* k, const void* v, void* o
 
 /*
  * flash_attn_fwd_strided -- flash_attn_fwd on strided views and any head dimension
- * d that is a multiple of 8 up to 128. The tensors are addressed as in the
+ * d that is a multiple of 8 up to 256. The tensors are addressed as in the
  * strided kernel interface of "6.1 FlashAttention V1 in detail", §8.3 (a stride
  * per batch, head and row for each of q, k, v, o; batch and head strides for the
  * row statistics), and a head dimension that is not a power of two is handled as
  * that section handles BLOCK_D > D: the kernel works on the next size it is built
- * for (64, 80, 96 or 128) with the positions past d masked, so they add nothing to
- * the scores and are never stored.
+ * for (64, 80, 96, 128 or 256) with the positions past d masked, so they add
+ * nothing to the scores and are never stored. Above 128 the 256-wide instance runs
+ * once per 128 columns of v and o (twice for d > 128).
  *
  * Element (b, h, i, c) of q is q[b*q_strides[0] + h*q_strides[1] + i*q_strides[2] + c]
  * (in elements of `dtype`; the head dimension is contiguous), likewise k, v and o;
@@ -146,7 +150,7 @@ int flash_attn_fwd_validate(const void* q, const void* k, const void* v, void* o
  * in increasing stride order every dimension of size > 1 steps past the span of
  * the dimensions inside it). Inputs may overlap each other and may repeat
  * (stride 0 shares one K/V head among all heads, for example). d must be a
- * multiple of 8 in [8, 128] (FA_ERR_HEADDIM). o and lse must not overlap any
+ * multiple of 8 in [8, 256] (FA_ERR_HEADDIM). o and lse must not overlap any
  * input's span (FA_ERR_ALIAS). Requires B * H * ceil(N / 256) < 2^31.
  */
 int flash_attn_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -249,7 +253,7 @@ int flash_attn_fwd_fp8_validate(const void* q8, const void* k8, const void* v8t,
  * there), up to rounding.
  *
  * Arguments q, k, v, o, lse, B, H, N, d, causal, scale, stream, dtype: as for
- * flash_attn_fwd.
+ * flash_attn_fwd, except that d is 64 or 128 (FA_ERR_HEADDIM otherwise).
  * num_splits : ranges per query tile. 0 chooses with flash_attn_fwd_splitkv_plan
  *           for the current device; values above the largest useful count (no
  *           empty range: the fewest 64-key tiles any query tile visits, at most
@@ -388,14 +392,15 @@ int flash_attn_bwd_validate(const void* q, const void* k, const void* v, const v
  * overlapped with the matrix products. FA_FWD_KERNEL_PIPELINED software-pipelines
  * each wave (scores of key tile t + 1 and the product of tile t - 1 around the
  * softmax of tile t); FA_FWD_KERNEL_PINGPONG lets the two waves of a SIMD alternate.
- * The ping-pong kernel serves d <= 64 and d in 97..128 (its 64- and 128-wide
- * instances); the pipelined kernel serves d in 65..96 (80- and 96-wide instances).
+ * The ping-pong kernel serves d <= 64, d in 97..128 and d in 129..256 (its 64-,
+ * 128- and 256-wide instances); the pipelined kernel serves d in 65..96 (80- and
+ * 96-wide instances).
  * The choice does not depend on N or the mask today; both arguments are checked
  * and kept so that it may. The environment variable FLASH_ATTN_FWD_KERNEL, read at
  * every call, forces one: "pipelined" or "pingpong" (then d in 65..96 runs the
- * ping-pong kernel's 128-wide instance).
+ * ping-pong kernel's 128-wide instance); d above 128 always takes the ping-pong kernel.
  * N     : sequence length, >= 0 (else FA_ERR_SHAPE).
- * d     : head dimension, a multiple of 8 in 8..128 (else FA_ERR_HEADDIM).
+ * d     : head dimension, a multiple of 8 in 8..256 (else FA_ERR_HEADDIM).
  * causal: 0 or 1 (else FA_ERR_ARG).
  * Returns FA_FWD_KERNEL_PIPELINED or FA_FWD_KERNEL_PINGPONG, or the negative status.
  * Makes no HIP call and keeps no state.
@@ -405,10 +410,10 @@ int flash_attn_fwd_kernel(int64_t N, int64_t d, int causal);
 /* Static, never-freed description of a status code (unknown codes included). */
 const char* flash_attn_strerror(int status);
 
-/* ABI version of this header, currently 8 (1: forward only; 2: + backward;
+/* ABI version of this header, currently 9 (1: forward only; 2: + backward;
  * 3: + key-split forward; 4: + strided forward; 5: + FP8 quantization and forward;
  * 6: + key-split forward without a caller workspace; 7: FP8 format argument, E5M2;
- * 8: + forward kernel query). */
+ * 8: + forward kernel query; 9: head dimensions up to 256 in the forward). */
 int flash_attn_abi_version(void);
 
 #ifdef __cplusplus

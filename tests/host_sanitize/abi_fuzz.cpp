@@ -21,6 +21,7 @@ namespace {
 int g_launches = 0;
 int g_kernel = 0;  // forward kernel of the last unsplit launch (FA_FWD_KERNEL_*)
 int g_fp8_d = 0;   // head dimension of the last FP8 launch
+int g_fwd_d = 0;   // instance width of the last ping-pong launch
 fa::FwdArgs g_fwd;
 }  // namespace
 
@@ -28,7 +29,10 @@ namespace fa {
 int rows_per_workgroup() { return 256; }
 int keys_per_tile() { return 64; }
 int device_cus() { return 256; }
-hipError_t launch_fwd(const FwdArgs& a, bool, int, bool, hipStream_t) {
+hipError_t launch_fwd(const FwdArgs& a, bool, int d, bool, hipStream_t) {
+  if (d != 64 && d != 128 && d != 256) std::abort();
+  if (d == 256 && a.splits > 1) std::abort();  // no key split at the wide instance
+  g_fwd_d = d;
   if (a.splits <= 1) g_kernel = FA_FWD_KERNEL_PINGPONG;
   g_fwd = a;
   ++g_launches;
@@ -112,7 +116,7 @@ void known_cases() {
   const uint64_t GB = 1ull << 30;
   void *q = base, *k = base + GB, *v = base + 2 * GB, *o = base + 3 * GB;
   float* lse = reinterpret_cast<float*>(base + 4 * GB);
-  CHECK(flash_attn_abi_version() == 8);
+  CHECK(flash_attn_abi_version() == 9);
   CHECK(flash_attn_fwd(q, k, v, o, lse, 2, 32, 4096, 128, 1, 0.088f, nullptr, FA_BF16) == FA_OK);
   CHECK(g_kernel == FA_FWD_KERNEL_PINGPONG && flash_attn_fwd_kernel(4096, 128, 1) == FA_FWD_KERNEL_PINGPONG);
   CHECK(flash_attn_fwd(q, k, v, o, lse, 1, 32, 16384, 128, 1, 0.088f, nullptr, FA_BF16) == FA_OK);
@@ -125,6 +129,12 @@ void known_cases() {
   CHECK(g_fwd.q_ext == 4096u * 128u * 2u && g_fwd.k_sh == 4096 * 128);
   CHECK(flash_attn_fwd(q, k, v, o, lse, 1, 1, 0, 128, 0, 0.1f, nullptr, FA_BF16) == FA_OK);
   CHECK(flash_attn_fwd(q, k, v, o, lse, 1, 1, 16, 96, 0, 0.1f, nullptr, FA_BF16) == FA_ERR_HEADDIM);
+  CHECK(flash_attn_fwd(q, k, v, o, lse, 2, 32, 4096, 256, 1, 0.0625f, nullptr, FA_BF16) == FA_OK);
+  CHECK(g_fwd_d == 256 && g_kernel == FA_FWD_KERNEL_PINGPONG && g_fwd.d_real == 256 && g_fwd.v_col0 == 0);
+  CHECK(flash_attn_fwd(q, k, v, o, lse, 1, 1, 16, 192, 0, 0.1f, nullptr, FA_BF16) == FA_ERR_HEADDIM);
+  CHECK(flash_attn_fwd_kernel(300, 200, 0) == FA_FWD_KERNEL_PINGPONG && flash_attn_fwd_kernel(1, 264, 0) == FA_ERR_HEADDIM);
+  CHECK(flash_attn_fwd_splitkv(q, k, v, o, lse, 1, 4, 4096, 256, 1, 0.1f, 4, base + 6 * GB, GB, nullptr, FA_BF16) ==
+        FA_ERR_HEADDIM);
   CHECK(flash_attn_fwd(q, k, v, q, lse, 1, 1, 16, 64, 0, 0.1f, nullptr, FA_BF16) == FA_ERR_ALIAS);
   CHECK(flash_attn_fwd(q, k, v, o, lse, 1, 1, 16, 64, 0, NAN, nullptr, FA_BF16) == FA_ERR_SCALE);
   CHECK(flash_attn_fwd(q, k, v, o, lse, (int64_t)1 << 40, 1, 16, 64, 0, 0.1f, nullptr, FA_BF16) == FA_ERR_SHAPE);

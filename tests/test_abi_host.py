@@ -50,7 +50,7 @@ def test_library_loads_and_exports_header_symbols():
 
 
 def test_abi_version_and_strerror():
-    assert fa.flash_attn_abi_version() == 8
+    assert fa.flash_attn_abi_version() == 9
     codes = [fa.FA_OK, fa.FA_ERR_NULL, fa.FA_ERR_SHAPE, fa.FA_ERR_HEADDIM, fa.FA_ERR_DTYPE,
              fa.FA_ERR_SCALE, fa.FA_ERR_ALIGN, fa.FA_ERR_ALIAS, fa.FA_ERR_HIP, fa.FA_ERR_ARG,
              fa.FA_ERR_WORKSPACE, fa.FA_ERR_STRIDE, fa.FA_ERR_SCRATCH]
@@ -66,7 +66,8 @@ def _args(q=A, k=A + GB, v=A + 2 * GB, o=A + 3 * GB, lse=A + 4 * GB, B=1, H=1, N
 
 BAD = [
     (dict(B=-1), fa.FA_ERR_SHAPE), (dict(H=-2), fa.FA_ERR_SHAPE), (dict(N=-5), fa.FA_ERR_SHAPE),
-    (dict(d=32), fa.FA_ERR_HEADDIM), (dict(d=96), fa.FA_ERR_HEADDIM), (dict(d=256), fa.FA_ERR_HEADDIM),
+    (dict(d=32), fa.FA_ERR_HEADDIM), (dict(d=96), fa.FA_ERR_HEADDIM), (dict(d=192), fa.FA_ERR_HEADDIM),
+    (dict(d=512), fa.FA_ERR_HEADDIM),
     (dict(dtype=2), fa.FA_ERR_DTYPE), (dict(dtype=-1), fa.FA_ERR_DTYPE),
     (dict(causal=2), fa.FA_ERR_ARG), (dict(causal=-1), fa.FA_ERR_ARG),
     (dict(scale=0.0), fa.FA_ERR_SCALE), (dict(scale=-0.5), fa.FA_ERR_SCALE),
@@ -96,7 +97,8 @@ def test_fwd_rejects_before_launch(kw, code):
 
 
 @pytest.mark.parametrize("kw", [dict(), dict(d=128, dtype=1, causal=1), dict(B=3, H=8, N=4099, d=128),
-                                dict(B=1, H=32, N=16384, d=128, causal=1)])
+                                dict(B=1, H=32, N=16384, d=128, causal=1), dict(d=256),
+                                dict(B=2, H=8, N=1000, d=256, causal=1, dtype=1)])
 def test_validate_accepts(kw):
     size = kw.get("B", 1) * kw.get("H", 1) * kw.get("N", 16) * kw.get("d", 64) * 2
     assert size < GB
@@ -256,6 +258,8 @@ BAD_SPLIT = [
     # the forward's own checks still apply
     (dict(d=96), fa.FA_ERR_HEADDIM), (dict(scale=0.0), fa.FA_ERR_SCALE), (dict(q=None), fa.FA_ERR_NULL),
     (dict(o=A), fa.FA_ERR_ALIAS), (dict(causal=5), fa.FA_ERR_ARG), (dict(dtype=7), fa.FA_ERR_DTYPE),
+    # the forward takes d = 256; the key split does not
+    (dict(d=256), fa.FA_ERR_HEADDIM),
 ]
 
 
@@ -317,6 +321,7 @@ def test_noalloc_scratch_size_matches_header_and_covers_the_planned_split():
 
 BAD_NOALLOC = [
     (dict(num_splits=-1), fa.FA_ERR_ARG), (dict(d=96), fa.FA_ERR_HEADDIM), (dict(scale=0.0), fa.FA_ERR_SCALE),
+    (dict(d=256), fa.FA_ERR_HEADDIM), (dict(d=256, num_splits=2), fa.FA_ERR_HEADDIM),
     (dict(q=None), fa.FA_ERR_NULL), (dict(o=A), fa.FA_ERR_ALIAS), (dict(causal=5), fa.FA_ERR_ARG),
     (dict(dtype=7), fa.FA_ERR_DTYPE), (dict(B=-1), fa.FA_ERR_SHAPE), (dict(lse=A + 4 * GB + 2), fa.FA_ERR_ALIGN),
     # 2 splits of B1 H64 N4096 d128 need 2 * 64 * 4096 * 129 * 4 bytes (258 MiB)
@@ -352,8 +357,8 @@ def _targs(q=A, k=A + GB, v=A + 2 * GB, o=A + 3 * GB, lse=A + 4 * GB, B=2, H=3, 
 
 
 BAD_STRIDED = [
-    (dict(d=12), fa.FA_ERR_HEADDIM), (dict(d=0), fa.FA_ERR_HEADDIM), (dict(d=136), fa.FA_ERR_HEADDIM),
-    (dict(d=4), fa.FA_ERR_HEADDIM),
+    (dict(d=12), fa.FA_ERR_HEADDIM), (dict(d=0), fa.FA_ERR_HEADDIM), (dict(d=264), fa.FA_ERR_HEADDIM),
+    (dict(d=4), fa.FA_ERR_HEADDIM), (dict(d=260), fa.FA_ERR_HEADDIM), (dict(d=512), fa.FA_ERR_HEADDIM),
     (dict(qs=(24000, 8000, 79)), fa.FA_ERR_STRIDE),          # row stride below d and not a multiple of 8
     (dict(ks=(24000, 8000, 72)), fa.FA_ERR_STRIDE),          # row stride below d
     (dict(vs=(24000, 8004, 80)), fa.FA_ERR_STRIDE),          # head stride not a multiple of 8
@@ -384,7 +389,7 @@ def test_strided_rejects_before_launch(kw, code):
 
 
 @pytest.mark.parametrize("kw", [
-    dict(), dict(d=8), dict(d=128), dict(d=64), dict(d=120),
+    dict(), dict(d=8), dict(d=128), dict(d=64), dict(d=120), dict(d=136), dict(d=200), dict(d=256),
     dict(qs=(100 * 3 * 3 * 80, 80, 3 * 3 * 80), ks=(100 * 3 * 3 * 80, 80, 3 * 3 * 80)),   # packed qkv rows
     dict(ks=(8000, 0, 80), vs=(8000, 0, 80)),                   # one K/V head shared by all heads
     dict(ks=(0, 0, 80), vs=(0, 0, 80)),                         # one K/V slice shared by everything
@@ -469,15 +474,16 @@ def test_fp8_accepts_and_empty():
                                    H=0)) == fa.FA_OK
 
 
-# (N, d, causal, kernel): the ping-pong kernel for d <= 64 and 97..128, the
-# pipelined kernel for d in 65..96, at any N and mask
+# (N, d, causal, kernel): the ping-pong kernel for d <= 64, 97..128 and 129..256,
+# the pipelined kernel for d in 65..96, at any N and mask
 PIPE, PING = _native.FA_FWD_KERNEL_PIPELINED, _native.FA_FWD_KERNEL_PINGPONG
 
 
 @pytest.mark.parametrize("N,d,causal,want", [
     (0, 64, 0, PING), (256, 64, 0, PING), (4096, 128, 0, PING), (4096, 128, 1, PING), (16384, 128, 1, PING),
     (65536, 128, 0, PING), (1024, 56, 0, PING), (300, 72, 1, PIPE), (300, 80, 0, PIPE), (300, 88, 1, PIPE),
-    (300, 96, 0, PIPE), (16384, 96, 1, PIPE), (300, 104, 0, PING), (8192, 8, 0, PING)])
+    (300, 96, 0, PIPE), (16384, 96, 1, PIPE), (300, 104, 0, PING), (8192, 8, 0, PING), (300, 136, 1, PING),
+    (4096, 256, 0, PING)])
 def test_fwd_kernel_choice(monkeypatch, N, d, causal, want):
     monkeypatch.delenv("FLASH_ATTN_FWD_KERNEL", raising=False)
     assert _native.fwd_kernel(N, d, causal) == want
@@ -490,11 +496,12 @@ def test_fwd_kernel_forced_and_rejects(monkeypatch):
     assert _native.fwd_kernel(300, 80, 0) == PING
     monkeypatch.setenv("FLASH_ATTN_FWD_KERNEL", "pipelined")
     assert _native.fwd_kernel(256, 64, 0) == PIPE
+    assert _native.fwd_kernel(256, 192, 0) == PING   # no pipelined instance above 128
     monkeypatch.setenv("FLASH_ATTN_FWD_KERNEL", "other")   # unknown names are ignored
     assert _native.fwd_kernel(256, 64, 0) == PING and _native.fwd_kernel(256, 80, 0) == PIPE
     monkeypatch.delenv("FLASH_ATTN_FWD_KERNEL")
     assert _native.fwd_kernel(-1, 64, 0) == fa.FA_ERR_SHAPE
-    for d in (0, 7, 12, 136):
+    for d in (0, 7, 12, 252, 264, 512):
         assert _native.fwd_kernel(256, d, 0) == fa.FA_ERR_HEADDIM
     assert _native.fwd_kernel(256, 64, 2) == fa.FA_ERR_ARG
     with pytest.raises(fa.FlashAttnError):
