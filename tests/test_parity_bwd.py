@@ -72,25 +72,33 @@ def _run_gpu(fa, bits, dtype, causal, scale):
     return conv(dq), conv(dk), conv(dv), conv(o)
 
 
-def _bounds(q, k, v, do, o16, scale, causal, dtype):
-    """Per-element error bounds (see the module docstring) for one slice [N, d]."""
+def _bounds(q, k, v, do, o16, scale, causal, dtype, row_block=2048):
+    """Per-element error bounds (see the module docstring) for one slice [N, d], over
+    blocks of complete query rows (dQ's bound per block, dK's and dV's summed over
+    the blocks) so that long slices need no N x N arrays."""
     u = UNIT[dtype]
     n, d = q.shape
-    s = scale * (q @ k.T)
-    if causal:
-        s = np.where(np.arange(n)[None, :] > np.arange(n)[:, None], -np.inf, s)
-    e = np.exp(s - s.max(axis=1, keepdims=True))
-    p = e / e.sum(axis=1, keepdims=True)
-    dp = do @ v.T
-    dlt = (dp * p).sum(axis=1)
-    ds = p * (dp - dlt[:, None])
-    dd = u * np.sum(np.abs(do * o16), axis=1)                       # D from the rounded O
-    dsc = 2.0 ** -24 * d * scale * (np.abs(q) @ np.abs(k).T) + 4e-6  # score and LSE error
     eta = UNDERFLOW[dtype]
-    err_ds = u * np.abs(ds) + eta + p * dd[:, None] + p * dsc * np.abs(dp - dlt[:, None])
-    b_dv = 4 * ((u * p + eta).T @ np.abs(do))
-    b_dq = 4 * scale * (err_ds @ np.abs(k))
-    b_dk = 4 * scale * (err_ds.T @ np.abs(q))
+    dd = u * np.sum(np.abs(do * o16), axis=1)                       # D from the rounded O
+    b_dq = np.zeros((n, d))
+    b_dk = np.zeros((n, d))
+    b_dv = np.zeros((n, d))
+    keys = np.arange(n)
+    for r0 in range(0, n, row_block):
+        rows = np.arange(r0, min(n, r0 + row_block))
+        s = scale * (q[rows] @ k.T)
+        if causal:
+            s = np.where(keys[None, :] > rows[:, None], -np.inf, s)
+        e = np.exp(s - s.max(axis=1, keepdims=True))
+        p = e / e.sum(axis=1, keepdims=True)
+        dp = do[rows] @ v.T
+        dlt = (dp * p).sum(axis=1)
+        ds = p * (dp - dlt[:, None])
+        dsc = 2.0 ** -24 * d * scale * (np.abs(q[rows]) @ np.abs(k).T) + 4e-6  # score and LSE error
+        err_ds = u * np.abs(ds) + eta + p * dd[rows, None] + p * dsc * np.abs(dp - dlt[:, None])
+        b_dv += 4 * ((u * p + eta).T @ np.abs(do[rows]))
+        b_dq[rows] = 4 * scale * (err_ds @ np.abs(k))
+        b_dk += 4 * scale * (err_ds.T @ np.abs(q[rows]))
     return b_dq, b_dk, b_dv
 
 
@@ -152,11 +160,20 @@ def test_workload_heads(fa, name, causal, heads):
 def test_long_context_invariants(fa):
     """B1 H32 N16384 d128 causal bf16: sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i
     (exact identities of the backward) on every head, within the summed bounds'
-    order of magnitude (4 u per term)."""
+    order of magnitude (4 u per term); and one complete head against the oracle
+    element by element, with the bounds of the module docstring."""
     w = inputs.WORKLOADS["longctx_b1_h32_n16384_d128_causal"]
     scale = float(np.float32(1.0 / math.sqrt(w.d)))
     bits = _draw(w.shape, w.dtype, w.sigma, w.seed)
-    gq, gk, gv, _ = _run_gpu(fa, bits, w.dtype, True, scale)
+    gq, gk, gv, go = _run_gpu(fa, bits, w.dtype, True, scale)
+    hh = 17
+    sl = [inputs.bits_to_f64(x, w.dtype).reshape(w.H, w.N, w.d)[hh] for x in bits]
+    rq, rk, rv, _ = attention_backward(*sl, scale, causal=True)
+    flat = lambda x: x.reshape(w.H, w.N, w.d)[hh]
+    b_dq, b_dk, b_dv = _bounds(*sl, flat(go), scale, True, w.dtype)
+    res = {n: _check(f"{n} head {hh}", flat(g), r, b, w.dtype)
+           for n, g, r, b in (("dq", gq, rq, b_dq), ("dk", gk, rk, b_dk), ("dv", gv, rv, b_dv))}
+    _log(f"bwd longctx head {hh} vs oracle: error / bound {res}")
     do = inputs.bits_to_f64(bits[3], w.dtype)
     u = UNIT[w.dtype]
     col_dk = gk.sum(axis=-2)
