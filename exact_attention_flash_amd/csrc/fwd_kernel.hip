@@ -25,7 +25,8 @@
 //    and VALU streams of the two waves sharing a SIMD overlap. One barrier per
 //    iteration publishes the next K/V tile.
 //  * K/V tiles are loaded straight into LDS with buffer_load ... lds (no staging
-//    registers) into a 3-stage ring, one tile ahead of use; the tile stream runs
+//    registers; the LDS address in M0 formed by the scalar unit from a per-wave
+//    offset) into a 3-stage ring, one tile ahead of use; the tile stream runs
 //    across work items, so the next item's first tile is in flight while the
 //    current item finishes. Q rows of an item take the same path into a fourth
 //    LDS region one item ahead (160 KiB of LDS in all). Rows past the end of the
@@ -39,10 +40,14 @@
 //  * Exponentials use exp2 with scale*log2(e) folded into one FMA per score.
 //  * Layout: q, k, v and o are addressed through (batch, head, row) strides with
 //    the head dimension contiguous. A head dimension d below the instance's D
-//    (64 or 128) is masked the way "6.1 FlashAttention V1 in detail", §8.3 masks
-//    BLOCK_D > D: chunks past d are loaded from an offset outside the buffer
+//    (64, 128 or 256) is masked the way "6.1 FlashAttention V1 in detail", §8.3
+//    masks BLOCK_D > D: chunks past d are loaded from an offset outside the buffer
 //    descriptor's range, which writes zeros into LDS, so they add nothing to the
 //    scores, and output columns past d are not stored.
+//  * The 256-wide instance forms the scores over all 256 columns but P V for one
+//    128-column half of V and O per launch (the host launches it once per half),
+//    and loads Q straight into registers, since 256 wide Q rows do not fit in LDS
+//    beside the K/V ring.
 //  * Causal: tiles past the workgroup's last row are never loaded; waves skip the
 //    math of tiles entirely after their rows; only tiles on the diagonal or at the
 //    end of the sequence evaluate the mask.
