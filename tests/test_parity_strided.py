@@ -325,3 +325,24 @@ def test_wide_headline_shape_d256(fa):
         assert_parity(mm, f"d=256 headline shape slice {s}")
         worst.append(mm["o_max_excess"])
     _log(f"d=256 headline shape, one row of each of {rows.size} work items: worst O excess {max(worst):.2e}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape,dtype,sigma", [
+    ((1, 1, 1, 256), inputs.BF16, 1.0),      # one query, one key
+    ((1, 1, 64, 256), inputs.FP16, 1.0),     # exactly one key tile
+    ((1, 3, 257, 192), inputs.BF16, 1.0),    # B*H = 3: no XCD grouping; one row past a query tile
+    ((2, 4, 130, 256), inputs.FP16, 8.0),    # sigma 8: extreme logits
+    ((1, 2, 700, 136), inputs.FP16, 8.0),
+])
+def test_wide_edge_shapes(fa, shape, dtype, sigma, causal):
+    d = shape[-1]
+    scale = _scale(d)
+    bits = inputs.draw_qkv(shape, dtype, sigma, 2000 + shape[2] + d + (1 if causal else 0))
+    q, k, v = (_dev_from_bits(x, dtype) for x in bits)
+    o, lse = fa.forward(q, k, v, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    ro, rl = _oracle(bits, dtype, causal, scale)
+    m = metrics(_o64(o, dtype), lse.double().cpu().numpy(), ro, rl, dtype)
+    _log(f"wide edge {shape} {dtype} sigma={sigma} causal={causal}: {m}")
+    assert_parity(m, f"wide edge {shape} causal={causal}")
