@@ -21,7 +21,9 @@
 //     (Q, dO, L and D) through LDS. Per tile each wave forms S = Q K^T and
 //     dP = dO V^T (K and V rows of its keys in registers), P and dS as above,
 //     and accumulates dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T through the
-//     transposing read).
+//     transposing read). The tile loop is software-pipelined: the S/dP products
+//     of tile j and the dV/dK products of tile j - 1 each run with half of a
+//     tile's P/dS work placed between them, one element per product or two.
 // All MFMAs are v_mfma_f32_32x32x16 on 16-bit operands with fp32 accumulation;
 // P and dS are rounded to the input dtype only as MFMA operands. Tiles are
 // loaded straight into LDS (buffer_load ... lds) into 4-stage rings with the
@@ -336,15 +338,42 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void bwd_dq(BwdArgs a) {
 
 // ------------------------------------------------------------------------------
 // 3. dK, dV: 4 waves x 32 keys, query tiles of 64 (Q, dO, L, D) streamed through LDS.
+//
+// One wave per SIMD, so nothing but the wave's own instruction order overlaps its
+// matrix work with its VALU work. The loop is software-pipelined over tiles: the
+// products of tile j (S and dP) and those of tile j - 1 (dV and dK) each run with
+// half of tile j's or tile j - 1's softmax work (P, dS and their 16-bit operands)
+// spread between them, one element or one packed operand after every product or
+// two. Per tile j the wave runs
+//   phase A(j): S and dP of tile j          | P, dS of tile j - 1, query block 1
+//   phase B(j): dV and dK of tile j - 1     | P, dS of tile j, query block 0
+// so that every VALU item reads products finished a phase earlier, and the LDS
+// ring holds tiles j - 1 (read by the dV/dK products), j, j + 1 and j + 2 (in
+// flight). Two register sets of per-tile values alternate between consecutive
+// tiles (the loop runs two tiles per trip), which keeps loop-carried values in
+// place without copies.
 constexpr int kKvWaves = 4;
-constexpr int kLookBwd = 3;  // LDS operand reads issued this many product steps ahead
 constexpr int kKvRows = 32 * kKvWaves;
+constexpr int kLookA = 4;  // row-operand reads of the S and dP products issued this many products ahead
+constexpr int kLookB = 3;  // transposing reads of the dV and dK products issued this many products ahead
+constexpr int kItems = 20;  // softmax items of one 32-row query block (16 elements, 4 packed operands)
+
+// Per-tile values of one wave: S and dP of the tile's two 32-row query blocks (P
+// and dS replace them in place), and P and dS rounded to 16 bits as the B operands
+// of the four 16-row k-steps of the dV and dK products.
+struct KvTile {
+  f32x16 s[2], dp[2];
+  u32x4 pb[4], dsb[4];
+};
 
 template <bool FP16, int D, bool CAUSAL>
 __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv(BwdArgs a) {
   using T = Tile<D>;
   constexpr int kStat = kTile * 4;                        // L or D of the tile's rows
   constexpr int kStage = 2 * T::bytes + 2 * kStat;        // Q, dO, L, D
+  constexpr int kSd = D / 16;                             // k-steps of one block's S (and dP) product
+  constexpr int kSlots = 4 * kSd;                         // products per phase (S/dP or dV/dK)
+  static_assert(kSlots == 8 * (D / 32), "both phases hold the same number of products");
   __shared__ __attribute__((aligned(1024))) char smem[kStages * kStage];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -354,7 +383,6 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv(BwdArgs a) {
   // workgroup -> (slice, key block): key blocks in increasing order, so under a
   // causal mask the heaviest blocks (most query tiles) start first
   const int bid = blockIdx.x;
-  const int k_blocks = (a.n + kKvRows - 1) / kKvRows;
   int bh, kb;
   if (a.xcd_grouped) {
     const int hpx = a.bh / 8;
@@ -365,7 +393,6 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv(BwdArgs a) {
     kb = bid / a.bh;
     bh = bid % a.bh;
   }
-  (void)k_blocks;
   const int N = a.n;
   const int k0 = kb * kKvRows;
   const int key0 = k0 + 32 * wave;  // this wave's first key
@@ -377,41 +404,46 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv(BwdArgs a) {
   const float* lg = a.lse + (int64_t)bh * N;
   const float* dg = a.delta + (int64_t)bh * N;
 
-  // query tiles that can see this workgroup's keys
+  // query tiles that can see this workgroup's keys (the first one starts at k0,
+  // a multiple of the tile height, under a causal mask)
   const int tiles_all = (N + kTile - 1) / kTile;
   const int t_first = CAUSAL ? k0 / kTile : 0;
   const int n_tiles = tiles_all - t_first;
 
+  // Tile loads: this wave's share of Q and dO (1 KiB blocks) and the tile's L and D
+  // rows (every wave loads them, the same bytes to the same place, so that all
+  // waves issue the same number of loads per tile). A tile past the last one is
+  // "loaded" through an empty buffer range (zeros into a free stage), which keeps
+  // the count of loads in flight the same on every trip.
   uint32_t ld_off[T::blocks / kKvWaves];
 #pragma unroll
   for (int i = 0; i < T::blocks / kKvWaves; ++i) ld_off[i] = T::src_offset(wave + kKvWaves * i, lane);
-  // every wave loads the tile's L and D rows (the same bytes to the same place), so
-  // that all waves issue the same number of loads per tile
-  // The kLoads loads of tile j, one at a time: load n < kLoads - 2 is Q block n / 2
-  // (even n) or dO block n / 2 (odd n) of this wave's share, then L and D.
+  const uint32_t lds_w = __builtin_amdgcn_readfirstlane(1024u * (uint32_t)wave);
   struct TileSrc {
     __amdgpu_buffer_rsrc_t q, o, l, d;
-    char* st;
+    uint32_t st;  // LDS byte address of the tile's stage
   };
   auto tile_src = [&](int j) {
     const int t = t_first + j;
+    const bool in = t < tiles_all;
     const uint32_t skip = (uint32_t)t * kTile * T::rowBytes;
     const uint32_t sskip = (uint32_t)t * kTile * 4;
-    return TileSrc{buffer_rsrc(qg + (int64_t)t * kTile * D, head_bytes - skip),
-                   buffer_rsrc(og + (int64_t)t * kTile * D, head_bytes - skip),
-                   buffer_rsrc(lg + t * kTile, (uint32_t)N * 4 - sskip),
-                   buffer_rsrc(dg + t * kTile, (uint32_t)N * 4 - sskip), smem + (j % kStages) * kStage};
+    const uint32_t rows = in ? head_bytes - skip : 0u, stats = in ? (uint32_t)N * 4 - sskip : 0u;
+    return TileSrc{buffer_rsrc(qg + (int64_t)t * kTile * D, rows), buffer_rsrc(og + (int64_t)t * kTile * D, rows),
+                   buffer_rsrc(lg + t * kTile, stats), buffer_rsrc(dg + t * kTile, stats),
+                   (uint32_t)(uintptr_t)smem + (uint32_t)((j % kStages) * kStage)};
   };
   constexpr int kLoads = 2 * T::blocks / kKvWaves + 2;
+  static_assert(kLoads <= kSlots, "one tile load per dV/dK product at most");
   auto issue_load = [&](const TileSrc& ts, int n) {
     if (n < kLoads - 2) {
       const int i = n >> 1;
-      if ((n & 1) == 0) buffer_load16_lds(ts.q, ld_off[i], ts.st + 1024 * (wave + kKvWaves * i));
-      else buffer_load16_lds(ts.o, ld_off[i], ts.st + T::bytes + 1024 * (wave + kKvWaves * i));
+      const uint32_t dst = ts.st + lds_w + 1024u * kKvWaves * i + ((n & 1) ? (uint32_t)T::bytes : 0u);
+      buffer_load16_lds_s((n & 1) ? ts.o : ts.q, ld_off[i], dst);
     } else if (n == kLoads - 2) {
-      buffer_load4_lds(ts.l, lane * 4, ts.st + 2 * T::bytes);
+      buffer_load4_lds_s(ts.l, lane * 4, ts.st + 2 * T::bytes);
     } else {
-      buffer_load4_lds(ts.d, lane * 4, ts.st + 2 * T::bytes + kStat);
+      buffer_load4_lds_s(ts.d, lane * 4, ts.st + 2 * T::bytes + kStat);
     }
   };
   auto issue_tile = [&](int j) {
@@ -421,7 +453,7 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv(BwdArgs a) {
   };
 
   issue_tile(0);
-  if (n_tiles > 1) issue_tile(1);
+  issue_tile(1);
   // K and V rows of this lane's key (B operands, k-slots d = 16 kk + 8 h + 0..7)
   u32x4 kreg[D / 16], vreg[D / 16];
   {
@@ -446,137 +478,188 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv(BwdArgs a) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) t_off[half][db] = T::tr_offset(lane, half, db);
 
+  // dK and dV accumulators, zeroed in the accumulation registers before the first
+  // product (the statement fixes where the zeroing happens)
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
     dk[db] = f32x16{};
     dv[db] = f32x16{};
+    asm volatile("" : "+a"(dk[db]), "+a"(dv[db]));
   }
 
-  for (int j = 0; j < n_tiles; ++j) {
-    // dK and dV stay in the accumulation registers across iterations (without this
-    // the loop-carried copy lands in vector registers and is copied every tile)
+  auto stage = [&](int j) -> const char* { return smem + (j % kStages) * kStage; };
+
+  // Softmax item i (0 .. kItems - 1) of query block b of tile j, held in x: items
+  // 0-7 and 10-17 are the elements 0-7 and 8-15 (rows 32 b + 8 g + 4 h + r for
+  // element 4 g + r): P = exp2(S scale log2 e - L log2 e), zero where the query
+  // precedes the key (MASK), and dS = P (dP - D) in place; items 8, 9 (18, 19) pack
+  // P and dS of elements 0-7 (8-15) into the B operand of k-step 2 b (2 b + 1).
+  // lim = key - (first query row of the tile) - 4 h: element 4 g + r is masked when
+  // 32 b + 8 g + r < lim.
+  auto item = [&](auto mask, KvTile& x, int b, int i, const f32x4 (&l4)[4], const f32x4 (&d4)[4], int lim) {
+    if (i == 8 || i == 18) {
+      x.pb[2 * b + i / 18] = pack_b<FP16>(x.s, 2 * b + i / 18);
+    } else if (i == 9 || i == 19) {
+      x.dsb[2 * b + i / 19] = pack_b<FP16>(x.dp, 2 * b + i / 19);
+    } else {
+      const int e = i < 8 ? i : i - 2, g = e >> 2, r = e & 3;
+      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(x.s[b][e], c, -l4[g][r] * kLog2e));
+      if constexpr (decltype(mask)::value) p = (32 * b + 8 * g + r < lim) ? 0.f : p;
+      x.s[b][e] = p;
+      x.dp[b][e] = p * (x.dp[b][e] - d4[g][r]);
+    }
+  };
+  // slot (product index within a phase) after which item i runs: the items start a
+  // few products into the phase (their L and D reads are then in) and spread evenly
+  auto item_slot = [](int i) {
+    constexpr int first = kSlots >= 32 ? 2 : 1;
+    return first + (i * (kSlots - first)) / kItems;
+  };
+  auto read_stats = [&](const char* st, int b, f32x4 (&l4)[4], f32x4 (&d4)[4]) {
+    const float* lt = reinterpret_cast<const float*>(st + 2 * T::bytes);
+    const float* dt = reinterpret_cast<const float*>(st + 2 * T::bytes + kStat);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      l4[g] = *reinterpret_cast<const f32x4*>(lt + 32 * b + 8 * g + 4 * h);
+      d4[g] = *reinterpret_cast<const f32x4*>(dt + 32 * b + 8 * g + 4 * h);
+    }
+  };
+
+  // Phase A(j): S and dP of tile j into cur (MFMA) | items of query block 1 of tile
+  // j - 1 in prev (VALU).
+  auto phase_a = [&](auto mfma, auto valu, auto mask, int j, KvTile& cur, KvTile& prev) {
+    constexpr bool kM = decltype(mfma)::value, kV = decltype(valu)::value;
+    const char* qt = stage(j);
+    const char* ot = qt + T::bytes;
+    u32x4 opa[kLookA + 1];
+    auto rd = [&](int m) {
+      const int b = m / (2 * kSd), kk = (m >> 1) % kSd;
+      opa[m % (kLookA + 1)] = lds_read16(((m & 1) ? ot : qt) + r_off[kk] + b * 32 * T::rowBytes);
+    };
+    if constexpr (kM) {
+#pragma unroll
+      for (int m = 0; m < kLookA; ++m) rd(m);
+    }
+    f32x4 l4[4], d4[4];
+    int lim = 0;
+    if constexpr (kV) {
+      read_stats(stage(j - 1), 1, l4, d4);
+      lim = key - (t_first + j - 1) * kTile - 4 * h;
+    }
+#pragma unroll
+    for (int m = 0; m < kSlots; ++m) {
+      if constexpr (kM) {
+        if (m + kLookA < kSlots) rd(m + kLookA);
+        __builtin_amdgcn_sched_barrier(0);
+        const int b = m / (2 * kSd), kk = (m >> 1) % kSd;
+        const u32x4 op = opa[m % (kLookA + 1)];
+        if (m & 1) {
+          if (kk == 0) cur.dp[b] = mfma32_va0<FP16>(op, vreg[0]);
+          else mfma32_va<FP16>(op, vreg[kk], cur.dp[b]);
+        } else {
+          if (kk == 0) cur.s[b] = mfma32_va0<FP16>(op, kreg[0]);
+          else mfma32_va<FP16>(op, kreg[kk], cur.s[b]);
+        }
+      }
+      if constexpr (kV) {
+#pragma unroll
+        for (int i = 0; i < kItems; ++i)
+          if (kM ? item_slot(i) == m : m == 0) item(mask, prev, 1, i, l4, d4, lim);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Phase B(j): dV and dK of tile j - 1 from prev (MFMA) | items of query block 0
+  // of tile j in cur (VALU) | the loads of tile j + 2.
+  auto phase_b = [&](auto mfma, auto valu, auto mask, int j, KvTile& cur, KvTile& prev, bool loads) {
+    constexpr bool kM = decltype(mfma)::value, kV = decltype(valu)::value;
+    const char* qp = stage(j - 1);
+    const char* op = qp + T::bytes;
+    u32x2 lo[kLookB + 1], hi[kLookB + 1];
+    auto rd = [&](int m) {
+      const int s = m >> 1, t = s / (D / 32), db = s % (D / 32), sl = m % (kLookB + 1);
+      const char* src = (m & 1) ? qp : op;
+      lo[sl] = lds_read_tr16(src + t_off[0][db] + 16 * t * T::rowBytes);
+      hi[sl] = lds_read_tr16(src + t_off[1][db] + 16 * t * T::rowBytes);
+    };
+    if constexpr (kM) {
+#pragma unroll
+      for (int m = 0; m < kLookB; ++m) rd(m);
+    }
+    f32x4 l4[4], d4[4];
+    int lim = 0;
+    if constexpr (kV) {
+      read_stats(stage(j), 0, l4, d4);
+      lim = key - (t_first + j) * kTile - 4 * h;
+    }
+    const TileSrc ts = tile_src(j + 2);
+#pragma unroll
+    for (int m = 0; m < kSlots; ++m) {
+      if constexpr (kM) {
+        if (m + kLookB < kSlots) rd(m + kLookB);
+        __builtin_amdgcn_sched_barrier(0);
+        const int s = m >> 1, t = s / (D / 32), db = s % (D / 32), sl = m % (kLookB + 1);
+        const u32x4 opnd = u32x4{lo[sl][0], lo[sl][1], hi[sl][0], hi[sl][1]};
+        if (m & 1) mfma32_aa<FP16>(opnd, prev.dsb[t], dk[db]);
+        else mfma32_aa<FP16>(opnd, prev.pb[t], dv[db]);
+      }
+      if (loads && m < kLoads) issue_load(ts, m);
+      if constexpr (kV) {
+#pragma unroll
+        for (int i = 0; i < kItems; ++i)
+          if (kM ? item_slot(i) == m : m == 0) item(mask, cur, 0, i, l4, d4, lim);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  using Y_ = std::true_type;
+  using N_ = std::false_type;
+  using MaskT = std::integral_constant<bool, CAUSAL>;
+  auto tile_end = [&]() {
+    wait_vmcnt<kLoads>();
+    __syncthreads();
+  };
+  // one pipelined trip: tile j into cur, tile j - 1 (in prev) finished
+  auto trip = [&](auto mask_a, auto mask_b, int j, KvTile& cur, KvTile& prev) {
+    // dK and dV stay in the accumulation registers across trips
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) asm volatile("" : "+a"(dk[db]), "+a"(dv[db]));
-    // tile j + kAhead: loaded one instruction per step of the dV/dK products (a
-    // load that waits for the address unit then holds up no product), or all at
-    // once here by a wave with no work in this tile
-    const bool load_next = j + kAhead < n_tiles;
-    const int qt0 = (t_first + j) * kTile;  // first query row of the tile
-    // queries below this wave's first key see none of its keys (causal)
-    const bool active = key0 < N && (!CAUSAL || qt0 + kTile - 1 >= key0);
-    if (!active && load_next) issue_tile(j + kAhead);
-    if (active) {
-      const char* qt = smem + (j % kStages) * kStage;
-      const char* ot = qt + T::bytes;
-      const float* lt = reinterpret_cast<const float*>(qt + 2 * T::bytes);
-      const float* dt = reinterpret_cast<const float*>(qt + 2 * T::bytes + kStat);
-      // The tile's 64 query rows form two blocks of 32. Products of block 0 run
-      // first; the VALU work of block 0 (P, dS and their 16-bit B operands) is
-      // interleaved with the S and dP products of block 1, and that of block 1
-      // with the dV and dK products of block 0, so that the exponentials run
-      // under matrix work instead of between its phases.
-      constexpr int kSd = D / 16;  // k-steps of one block's S (and dP) product
-      f32x16 s[2], dp[2];
-      u32x4 pb[4], dsb[4];
-      // P and dS in place for query rows 32 b + 8 g + 4 h + r (r = 0..3)
-      const bool masked = CAUSAL && qt0 < key0 + 31;
-      auto p_ds = [&](int b, int g) {
-        const int row = 32 * b + 8 * g + 4 * h;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lt + row);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dt + row);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int e = 4 * g + r;
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][e], c, -l4[r] * kLog2e));
-          if (masked && qt0 + row + r < key) p = 0.f;
-          s[b][e] = p;
-          dp[b][e] = p * (dp[b][e] - d4[r]);
-        }
-      };
-      // VALU job j of block b: 0..3 P and dS of one row group, 4 and 5 the B operands
-      auto valu_job = [&](int b, int j) {
-        if (j < 4) {
-          p_ds(b, j);
-        } else if (j == 4) {
-          pb[2 * b] = pack_b<FP16>(s, 2 * b);
-          pb[2 * b + 1] = pack_b<FP16>(s, 2 * b + 1);
-        } else {
-          dsb[2 * b] = pack_b<FP16>(dp, 2 * b);
-          dsb[2 * b + 1] = pack_b<FP16>(dp, 2 * b + 1);
-        }
-      };
-      // the jobs of a block run after steps 1 .. kSd - 1 of the next product phase;
-      // the first reads accumulators that the products just before may still be
-      // writing: mfma_wait() supplies the wait states (the results pass through it,
-      // so no read is scheduled earlier)
-      auto jobs_after_step = [&](int b, int k) {
-        if (k == 1) mfma_wait(s[b], dp[b]);
-#pragma unroll
-        for (int jj = 0; jj < 6; ++jj)
-          if ((jj + 1 < kSd ? jj + 1 : kSd - 1) == k) valu_job(b, jj);
-      };
-      // S = Q K^T and dP = dO V^T, block 0 then block 1, D/16 k-steps each; operand
-      // reads from LDS are issued kLookBwd steps ahead of their products
-      {
-        u32x4 qa[kLookBwd + 1], oa[kLookBwd + 1];
-        auto issue = [&](int st) {
-          const int kk = st % kSd, b = st / kSd;
-          qa[st % (kLookBwd + 1)] = lds_read16(qt + r_off[kk] + b * 32 * T::rowBytes);
-          oa[st % (kLookBwd + 1)] = lds_read16(ot + r_off[kk] + b * 32 * T::rowBytes);
-        };
-#pragma unroll
-        for (int st = 0; st < kLookBwd; ++st) issue(st);
-#pragma unroll
-        for (int st = 0; st < 2 * kSd; ++st) {
-          if (st + kLookBwd < 2 * kSd) issue(st + kLookBwd);
-          __builtin_amdgcn_sched_barrier(0);
-          const int kk = st % kSd, b = st / kSd, sl = st % (kLookBwd + 1);
-          if (kk == 0) {
-            s[b] = mfma32_va0<FP16>(qa[sl], kreg[kk]);
-            dp[b] = mfma32_va0<FP16>(oa[sl], vreg[kk]);
-          } else {
-            mfma32_va<FP16>(qa[sl], kreg[kk], s[b]);
-            mfma32_va<FP16>(oa[sl], vreg[kk], dp[b]);
-          }
-          if (b == 1) jobs_after_step(0, kk);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      // dV^T += dO^T P and dK^T += Q^T dS: k-steps t = 0, 1 take block 0's rows
-      // (the first kSd steps), t = 2, 3 block 1's
-      {
-        u32x2 olo[kLookBwd + 1], ohi[kLookBwd + 1], qlo[kLookBwd + 1], qhi[kLookBwd + 1];
-        static_assert(kLoads <= D / 8, "one tile load per dV/dK step");
-        const TileSrc ts = tile_src(load_next ? j + kAhead : j);
-        auto issue = [&](int st) {
-          const int t = st / (D / 32), db = st % (D / 32), sl = st % (kLookBwd + 1);
-          olo[sl] = lds_read_tr16(ot + t_off[0][db] + 16 * t * T::rowBytes);
-          ohi[sl] = lds_read_tr16(ot + t_off[1][db] + 16 * t * T::rowBytes);
-          qlo[sl] = lds_read_tr16(qt + t_off[0][db] + 16 * t * T::rowBytes);
-          qhi[sl] = lds_read_tr16(qt + t_off[1][db] + 16 * t * T::rowBytes);
-        };
-#pragma unroll
-        for (int st = 0; st < kLookBwd; ++st) issue(st);
-#pragma unroll
-        for (int st = 0; st < D / 8; ++st) {
-          if (st + kLookBwd < D / 8) issue(st + kLookBwd);
-          __builtin_amdgcn_sched_barrier(0);
-          const int t = st / (D / 32), db = st % (D / 32), sl = st % (kLookBwd + 1);
-          mfma32_aa<FP16>(u32x4{olo[sl][0], olo[sl][1], ohi[sl][0], ohi[sl][1]}, pb[t], dv[db]);
-          mfma32_aa<FP16>(u32x4{qlo[sl][0], qlo[sl][1], qhi[sl][0], qhi[sl][1]}, dsb[t], dk[db]);
-          if (st < kLoads && load_next) issue_load(ts, st);
-          if (st < kSd) jobs_after_step(1, st);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-    }
-    if (j + 1 < n_tiles) {
-      if (j + kAhead < n_tiles) wait_vmcnt<kLoads>();
-      else wait_vmcnt<0>();
-      __syncthreads();
-    }
+    phase_a(Y_{}, Y_{}, mask_a, j, cur, prev);
+    phase_b(Y_{}, Y_{}, mask_b, j, cur, prev, true);
+    tile_end();
+  };
+  // the last tile (in x): its block-1 items, then its dV and dK products
+  auto finish = [&](int j, KvTile& x) {
+    // no load may still be writing LDS when the workgroup ends
+    wait_vmcnt<0>();
+    mfma_wait(x.s[1], x.dp[1]);
+    phase_a(N_{}, Y_{}, MaskT{}, j + 1, x, x);
+    phase_b(Y_{}, N_{}, MaskT{}, j + 1, x, x, false);
+  };
+
+  KvTile X, Y;
+  // tile 0: its S and dP products, then its block-0 items with nothing to overlap
+  phase_a(Y_{}, N_{}, N_{}, 0, X, Y);
+  mfma_wait(X.s[0], X.dp[0]);
+  phase_b(N_{}, Y_{}, MaskT{}, 0, X, Y, true);
+  tile_end();
+  // Trips run in pairs (tiles j in Y, j + 1 in X), at least one pair, so that the
+  // last tile is always in X and the code has a single path: tiles past the end
+  // (one for an even tile count, two for a single tile) read Q, dO, L and D as
+  // zeros (P = 1, dS = 0, dO = 0: they add exactly nothing). Under a causal mask the
+  // items of tiles 0 and 1 (the first pair) need the mask; from tile 2 on every
+  // query of a tile follows every key of the block.
+  const int pairs = max(1, n_tiles >> 1);
+  trip(MaskT{}, MaskT{}, 1, Y, X);
+  trip(MaskT{}, N_{}, 2, X, Y);
+  for (int p = 1; p < pairs; ++p) {
+    trip(N_{}, N_{}, 2 * p + 1, Y, X);
+    trip(N_{}, N_{}, 2 * p + 2, X, Y);
   }
+  finish(2 * pairs, X);
 
   mfma_drain_a<D / 32>(dk, dv);
   if (key < N) {

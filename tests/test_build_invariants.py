@@ -7,8 +7,8 @@ because the compiler's hazard checks do not see an MFMA inside an asm statement.
 That is sound only while the compiler neither spills nor moves those registers
 inside the tile loop: a copy or spill placed right after such a product would
 read its result before the product has finished. These tests compile the kernel
-to assembly (CPU only; hipcc cross-compiles) and check that every basic block
-holding matrix products is free of register-file moves and scratch accesses.
+to assembly (CPU only; hipcc cross-compiles) and check that no register-file
+move or scratch access sits between two matrix products of a basic block.
 
 The direct-to-LDS loads are inline assembly too, and read scalar registers (the
 buffer descriptor, M0) that a VALU instruction may have written just before; the
@@ -69,10 +69,15 @@ def test_dkdv_product_blocks_have_no_moves_or_spills():
     assert len(kernels) == 8  # {bf16, fp16} x {64, 128} x {causal, not}
     for k in kernels:
         for name, ins in _blocks(asm, k):
-            if not any("mfma" in i for i in ins):
+            at = [n for n, i in enumerate(ins) if "mfma" in i]
+            if not at:
                 continue
-            moves = [i for i in ins if "accvgpr" in i or i.startswith("scratch_")]
-            assert not moves, f"{k} block {name}: {len(moves)} register moves/spills beside asm products"
+            # set-up before the block's first product (K and V into the accumulation
+            # registers, dK and dV zeroed) and the read-out after its last one (after
+            # the drain) are allowed; the wait-state audit below checks those moves
+            # as VALU accesses like any other
+            moves = [i for i in ins[at[0]:at[-1]] if "accvgpr" in i or i.startswith("scratch_")]
+            assert not moves, f"{k} block {name}: {len(moves)} register moves/spills between asm products"
 
 
 # ---- wait states around instructions the compiler cannot see inside inline asm ----
