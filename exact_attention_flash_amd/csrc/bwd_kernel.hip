@@ -46,6 +46,13 @@ namespace bwd {
 
 using namespace ::fa::ops;
 
+// The 4-byte load straight to LDS with a scalar LDS byte address, under the rules of
+// buffer_load16_lds_s (one wait state after a scalar write of M0; neither M0 nor the
+// descriptor written by a VALU instruction within five).
+__device__ __forceinline__ void buffer_load4_lds_s(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t lds_addr) {
+  asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(lds_addr) : "memory");
+}
+
 constexpr int kStages = 4;
 constexpr int kAhead = 2;
 constexpr int kTile = 64;  // rows of a streamed tile (keys in bwd_dq, queries in bwd_dkdv)

@@ -126,12 +126,6 @@ __device__ __forceinline__ void buffer_load4_lds(__amdgpu_buffer_rsrc_t r, uint3
   asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(m0) : "memory");
 }
 
-// The 4-byte load with a scalar LDS byte address, under the same rules as
-// buffer_load16_lds_s.
-__device__ __forceinline__ void buffer_load4_lds_s(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t lds_addr) {
-  asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(lds_addr) : "memory");
-}
-
 // s_waitcnt on the vector-memory counter only (gfx9 encoding: expcnt and lgkmcnt at max).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
