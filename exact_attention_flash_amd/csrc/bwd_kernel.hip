@@ -9,13 +9,14 @@
 // with D_i = rowsum(dO ∘ O)_i (the identity rowsum(dP ∘ P) = rowsum(dO ∘ O) of
 // V1 §6.1). Three kernels run in order on one stream:
 //  1. bwd_delta: D = rowsum(dO ∘ O) in fp32, one value per query row.
-//  2. bwd_dq: a workgroup owns 256 query rows (8 waves of 32) and streams key
-//     tiles of 64 rows through LDS, like the forward pass. Per tile each wave
-//     forms S^T = K Q^T and dP^T = V dO^T (MFMA, operands K and V rows from LDS,
-//     Q and dO rows in registers), P^T = exp2(S^T scale log2 e - L log2 e),
+//  2. bwd_dq: a workgroup owns 256 query rows (4 waves of 64, one wave per SIMD)
+//     and streams key sub-tiles of 32 rows through LDS. Per sub-tile each wave
+//     forms S^T = K Q^T and dP^T = V dO^T for its two 32-row query blocks (MFMA,
+//     operands K and V rows from LDS, each read serving both blocks; Q and dO
+//     rows in registers), P^T = exp2(S^T scale log2 e - L log2 e),
 //     dS^T = P^T ∘ (dP^T - D), and accumulates dQ^T += K^T dS^T with K^T read
 //     through the transposing LDS read and dS^T rounded to 16 bits as the B
-//     operand without leaving registers.
+//     operand without leaving registers; software-pipelined like bwd_dkdv.
 //  3. bwd_dkdv: a workgroup owns 128 keys (4 waves of 32, one wave per SIMD, so
 //     each wave has the whole register file) and streams query tiles of 64 rows
 //     (Q, dO, L and D) through LDS. Per tile each wave forms S = Q K^T and
@@ -30,8 +31,8 @@
 // same XOR chunk swizzle as the forward pass, so every operand read hits every
 // LDS bank once. Rows past N read as zeros through the buffer descriptor range;
 // their contributions vanish because their K, V (dQ kernel) or Q, dO (dK/dV
-// kernel) rows are zero, and keys past N are masked in the dQ kernel so that no
-// overflowing exponent can reach a valid row.
+// kernel) rows are zero, and keys past N (sub-tiles past the end included) are
+// masked in the dQ kernel so that no overflowing exponent can reach a valid row.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -58,12 +59,12 @@ constexpr int kAhead = 2;
 constexpr int kTile = 64;  // rows of a streamed tile (keys in bwd_dq, queries in bwd_dkdv)
 constexpr float kLog2e = 1.4426950408889634074f;
 
-// Row-major 64-row tile of D-element rows in LDS (16-byte chunks swizzled by row).
-template <int D>
+// Row-major tile of ROWS D-element rows in LDS (16-byte chunks swizzled by row).
+template <int D, int ROWS = kTile>
 struct Tile {
   static constexpr int rowBytes = D * 2;
   static constexpr int chunksPerRow = D / 8;
-  static constexpr int bytes = kTile * rowBytes;
+  static constexpr int bytes = ROWS * rowBytes;
   static constexpr int blocks = bytes / 1024;  // 1 KiB per wave-instruction
   // lane `lane` of 1 KiB block b lands at chunk position 64 b + lane = (row, physical
   // chunk) and fetches the logical chunk physical ^ swizzle(row) of that row
@@ -198,19 +199,52 @@ __global__ __launch_bounds__(256) void bwd_delta(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------------------
-// 2. dQ: 8 waves x 32 query rows, key tiles of 64 streamed through LDS.
-constexpr int kDqWaves = 8;
-constexpr int kDqRows = 32 * kDqWaves;
+// 2. dQ: 4 waves x 64 query rows (one wave per SIMD), key sub-tiles of 32 streamed
+// through LDS.
+//
+// Each wave owns two 32-row query blocks, so every K, V or K^T operand it reads
+// from LDS serves two products (one per block): half the LDS bytes per product of
+// one block per wave. The blocks' Q and dO rows (the B operands of S^T and dP^T)
+// and the dQ^T accumulators fill the accumulation registers; with S^T = K Q^T the
+// lane is the query, so L and D are per-lane constants. The sub-tile loop is
+// software-pipelined like the dK/dV kernel's tile loop:
+//   phase A(j): S^T and dP^T of sub-tile j (both blocks)  | P, dS of sub-tile j - 1, block 1
+//   phase B(j): dQ^T of sub-tile j - 1 (both blocks)       | P, dS of sub-tile j, block 0
+constexpr int kDqWaves = 4;
+constexpr int kDqRows = 64 * kDqWaves;
+constexpr int kSub = 32;        // keys per sub-tile
+constexpr int kDqStages = 4;
+constexpr int kDqItems = 18;    // softmax items of one block: 16 elements, 2 packed dS operands
+
+// Per-sub-tile values of one wave: S^T and dP^T of its two query blocks (dS^T
+// replaces dP^T in place) and dS^T rounded to 16 bits as the B operands of the two
+// 16-key k-steps of the dQ^T product.
+struct DqSub {
+  f32x16 s[2], dp[2];
+  u32x4 dsb[2][2];
+};
+
+template <bool FP16>
+__device__ __forceinline__ u32x4 pack_b1(const f32x16& v, int t) {
+  const int o = 8 * t;
+  return u32x4{pack2<FP16>(v[o], v[o + 1]), pack2<FP16>(v[o + 2], v[o + 3]), pack2<FP16>(v[o + 4], v[o + 5]),
+               pack2<FP16>(v[o + 6], v[o + 7])};
+}
 
 template <bool FP16, int D, bool CAUSAL>
 __global__ __launch_bounds__(64 * kDqWaves, 1) void bwd_dq(BwdArgs a) {
-  using T = Tile<D>;
+  using T = Tile<D, kSub>;
   constexpr int kStage = 2 * T::bytes;  // K then V
-  __shared__ __attribute__((aligned(1024))) char smem[kStages * kStage];
+  constexpr int kSd = D / 16;           // k-steps of S^T (and dP^T)
+  constexpr int kSlotsA = 4 * kSd;      // S^T, dP^T products of both blocks
+  constexpr int kSlotsB = 4 * (D / 32); // dQ^T products: 2 k-steps x D/32 blocks x 2 query blocks
+  constexpr int kLoads = 2 * T::blocks / kDqWaves;
+  static_assert(T::blocks % kDqWaves == 0 && kLoads <= kSlotsB, "tile loads");
+  __shared__ __attribute__((aligned(1024))) char smem[kDqStages * kStage];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave >> 2, h = lane >> 5, l32 = lane & 31;
+  const int h = lane >> 5, l32 = lane & 31;
 
   // workgroup -> (slice, query tile): heaviest causal tiles first; with
   // xcd_grouped all query tiles of a slice on one XCD (shared K/V in its L2)
@@ -234,113 +268,248 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void bwd_dq(BwdArgs a) {
   const uint16_t* kg = reinterpret_cast<const uint16_t*>(a.k) + head;
   const uint16_t* vg = reinterpret_cast<const uint16_t*>(a.v) + head;
 
-  // rows of this wave: block wave%4 (waves 0-3) or 7 - wave%4 (waves 4-7), so that
-  // causal work on the diagonal tiles is spread over the SIMDs
-  const int row0 = q0 + 32 * (grp == 0 ? (wave & 3) : 7 - (wave & 3));
-  const int qrow = row0 + l32;
-  const int tiles_all = (N + kTile - 1) / kTile;
-  const int n_tiles = CAUSAL ? min(tiles_all, (min(q0 + kDqRows, N) - 1) / kTile + 1) : tiles_all;
+  // query blocks of this wave: 32-row blocks wave and 7 - wave of the tile, so that
+  // the causal diagonal's masked work is spread evenly over the waves
+  int qrow[2];
+  qrow[0] = q0 + 32 * wave + l32;
+  qrow[1] = q0 + 32 * (2 * kDqWaves - 1 - wave) + l32;
 
+  // key sub-tiles: those any row of the tile can see; from sub-tile m0 on some
+  // element needs the mask (causal diagonal, keys past N)
+  const int subs_all = (N + kSub - 1) / kSub;
+  const int n_sub = CAUSAL ? (min(q0 + kDqRows, N) + kSub - 1) / kSub : subs_all;
+  const int m0 = CAUSAL ? q0 / kSub : (N % kSub == 0 ? n_sub : n_sub - 1);
+
+  // sub-tile loads: this wave's share of K and V (1 KiB blocks); a sub-tile past the
+  // last one reads zeros through an empty range (its keys are masked)
   uint32_t ld_off[T::blocks / kDqWaves];
 #pragma unroll
   for (int i = 0; i < T::blocks / kDqWaves; ++i) ld_off[i] = T::src_offset(wave + kDqWaves * i, lane);
-  auto issue_tile = [&](int t) {
-    const uint32_t skip = (uint32_t)t * kTile * T::rowBytes;
-    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(kg + (int64_t)t * kTile * D, head_bytes - skip);
-    const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(vg + (int64_t)t * kTile * D, head_bytes - skip);
-    char* st = smem + (t % kStages) * kStage;
-#pragma unroll
-    for (int i = 0; i < T::blocks / kDqWaves; ++i) {
-      buffer_load16_lds(kr, ld_off[i], st + 1024 * (wave + kDqWaves * i));
-      buffer_load16_lds(vr, ld_off[i], st + T::bytes + 1024 * (wave + kDqWaves * i));
-    }
+  const uint32_t lds_w = __builtin_amdgcn_readfirstlane(1024u * (uint32_t)wave);
+  struct SubSrc {
+    __amdgpu_buffer_rsrc_t k, v;
+    uint32_t st;
   };
-  constexpr int kLoads = 2 * T::blocks / kDqWaves;
+  auto sub_src = [&](int j) {
+    const bool in = j < subs_all;
+    const uint32_t skip = (uint32_t)j * kSub * T::rowBytes;
+    const uint32_t rows = in ? head_bytes - skip : 0u;
+    return SubSrc{buffer_rsrc(kg + (int64_t)j * kSub * D, rows), buffer_rsrc(vg + (int64_t)j * kSub * D, rows),
+                  (uint32_t)(uintptr_t)smem + (uint32_t)((j % kDqStages) * kStage) + lds_w};
+  };
+  auto issue_load = [&](const SubSrc& ss, int n) {
+    const int i = n >> 1;
+    const uint32_t dst = ss.st + 1024u * kDqWaves * i + ((n & 1) ? (uint32_t)T::bytes : 0u);
+    buffer_load16_lds_s((n & 1) ? ss.v : ss.k, ld_off[i], dst);
+  };
+  auto issue_sub = [&](int j) {
+    const SubSrc ss = sub_src(j);
+#pragma unroll
+    for (int n = 0; n < kLoads; ++n) issue_load(ss, n);
+  };
 
-  issue_tile(0);
-  if (n_tiles > 1) issue_tile(1);
-  // Q and dO rows of this lane's query (B operands, k-slots d = 16 kk + 8 h + 0..7),
-  // L and D of the query (rows past N read as zeros and are never stored)
-  u32x4 qreg[D / 16], doreg[D / 16];
+  issue_sub(0);
+  issue_sub(1);
+  // Q and dO rows of this lane's queries (B operands, k-slots d = 16 kk + 8 h + 0..7),
+  // L log2 e and D of the queries (rows past N read as zeros and are never stored)
+  u32x4 qreg[2][kSd], oreg[2][kSd];
+  float lse2[2], dlt[2];
   {
     const __amdgpu_buffer_rsrc_t qr = buffer_rsrc(reinterpret_cast<const uint16_t*>(a.q) + head, head_bytes);
     const __amdgpu_buffer_rsrc_t dr = buffer_rsrc(reinterpret_cast<const uint16_t*>(a.dout) + head, head_bytes);
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      qreg[kk] = buffer_load16(qr, (uint32_t)qrow * T::rowBytes + kk * 32 + h * 16);
-      doreg[kk] = buffer_load16(dr, (uint32_t)qrow * T::rowBytes + kk * 32 + h * 16);
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int kk = 0; kk < kSd; ++kk) {
+        qreg[qb][kk] = buffer_load16(qr, (uint32_t)qrow[qb] * T::rowBytes + kk * 32 + h * 16);
+        oreg[qb][kk] = buffer_load16(dr, (uint32_t)qrow[qb] * T::rowBytes + kk * 32 + h * 16);
+      }
+      const bool ok = qrow[qb] < N;
+      lse2[qb] = ok ? a.lse[(int64_t)bh * N + qrow[qb]] * kLog2e : 0.f;
+      dlt[qb] = ok ? a.delta[(int64_t)bh * N + qrow[qb]] : 0.f;
     }
   }
-  const bool row_ok = qrow < N;
-  const float lse2 = row_ok ? a.lse[(int64_t)bh * N + qrow] * kLog2e : 0.f;
-  const float dlt = row_ok ? a.delta[(int64_t)bh * N + qrow] : 0.f;
   const float c = a.scale_log2;
   wait_vmcnt<0>();
   __syncthreads();
 
-  int k_off[D / 16];
+  int k_off[kSd];
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) k_off[kk] = T::row_offset(l32, h, kk);
+  for (int kk = 0; kk < kSd; ++kk) k_off[kk] = T::row_offset(l32, h, kk);
   int t_off[2][D / 32];
 #pragma unroll
   for (int half = 0; half < 2; ++half)
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) t_off[half][db] = T::tr_offset(lane, half, db);
 
-  f32x16 dq[D / 32];
+  // dQ^T accumulators (one lane per query), zeroed in the accumulation registers
+  // before the first product
+  f32x16 dq[2][D / 32];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) dq[db] = f32x16{};
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      dq[qb][db] = f32x16{};
+      asm volatile("" : "+a"(dq[qb][db]));
+    }
 
-  for (int i = 0; i < n_tiles; ++i) {
-    if (i + kAhead < n_tiles) issue_tile(i + kAhead);
-    const bool active = row0 < N && (!CAUSAL || i * kTile <= row0 + 31);
-    if (active) {
-      const char* kt = smem + (i % kStages) * kStage;
-      const char* vt = kt + T::bytes;
-      // S^T = K Q^T and dP^T = V dO^T: two key blocks of 32, D/16 k-steps each
-      f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+  auto stage = [&](int j) -> const char* { return smem + (j % kDqStages) * kStage; };
+  // the last key a query row of block qb may see (causal), or the last key
+  const int lim0 = CAUSAL ? min(qrow[0], N - 1) : N - 1;
+  const int lim1 = CAUSAL ? min(qrow[1], N - 1) : N - 1;
+
+  // Softmax item i of block qb of sub-tile j in x: items 0-7 and 9-16 are elements
+  // 0-7 and 8-15 (key 8 g + 4 h + r of the sub-tile for element 4 g + r): P =
+  // exp2(S scale log2 e - L log2 e), zero for keys past the row's last (MASK), and
+  // dS = P (dP - D) in place; items 8 and 17 pack dS of elements 0-7 (8-15) into the
+  // B operand of k-step 0 (1). lim = last visible key - first key of the sub-tile -
+  // 4 h: element 4 g + r is masked when 8 g + r > lim.
+  auto item = [&](auto mask, DqSub& x, int qb, int i, int lim) {
+    if (i == 8 || i == 17) {
+      x.dsb[qb][i / 17] = pack_b1<FP16>(x.dp[qb], i / 17);
+    } else {
+      const int e = i < 8 ? i : i - 1, g = e >> 2, r = e & 3;
+      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(x.s[qb][e], c, -lse2[qb]));
+      if constexpr (decltype(mask)::value) p = (8 * g + r > lim) ? 0.f : p;
+      x.dp[qb][e] = p * (x.dp[qb][e] - dlt[qb]);
+    }
+  };
+  // slot after which item i runs in a phase of `slots` products, from product
+  // `first` on: phase A's items (a sub-tile finished a phase earlier) start after
+  // two products; phase B's read block 0's products, the last of which ends a few
+  // products before phase A does, so they start after four
+  auto item_slot = [](int i, int slots, int first) { return first + (i * (slots - first)) / kDqItems; };
+
+  // Phase A(j): S^T and dP^T of sub-tile j into cur (MFMA) | items of block 1 of
+  // sub-tile j - 1 in prev (VALU). Product m: k-step m / 4; m % 4 = S^T of block 0,
+  // of block 1, dP^T of block 0, of block 1. The K row read of a k-step serves its
+  // two S^T products, the V row read its two dP^T products.
+  constexpr int kLookRA = 3;  // operand reads issued this many reads ahead
+  auto phase_a = [&](auto mfma, auto valu, auto mask, int j, DqSub& cur, DqSub& prev) {
+    constexpr bool kM = decltype(mfma)::value, kV = decltype(valu)::value;
+    const char* kt = stage(j);
+    const char* vt = kt + T::bytes;
+    u32x4 opa[kLookRA + 1];
+    auto rd = [&](int r) {  // read r: k-step r / 2, K (even) or V (odd)
+      opa[r % (kLookRA + 1)] = lds_read16(((r & 1) ? vt : kt) + k_off[r >> 1]);
+    };
+    if constexpr (kM) {
 #pragma unroll
-      for (int st = 0; st < D / 8; ++st) {
-        const int kk = st >> 1, b = st & 1;
-        const u32x4 ka = lds_read16(kt + k_off[kk] + b * 32 * T::rowBytes);
-        const u32x4 va = lds_read16(vt + k_off[kk] + b * 32 * T::rowBytes);
-        s[b] = mfma32<FP16>(ka, qreg[kk], s[b]);
-        dp[b] = mfma32<FP16>(va, doreg[kk], dp[b]);
-      }
-      // P^T and dS^T; key = 32 b + 8 (r / 4) + 4 h + r % 4 within the tile
-      const int kv0 = i * kTile;
-      const bool masked = (kv0 + kTile > N) || (CAUSAL && kv0 + kTile - 1 > row0);
-      int lim = N - 1 - kv0;
-      if (CAUSAL) lim = min(lim, qrow - kv0);
-      lim -= 4 * h;
+      for (int r = 0; r < kLookRA; ++r) rd(r);
+    }
+    const int lim = (kV ? lim1 : 0) - (j - 1) * kSub - 4 * h;
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], c, -lse2));
-          if (masked && 32 * b + 8 * (r >> 2) + (r & 3) > lim) p = 0.f;
-          s[b][r] = p * (dp[b][r] - dlt);
+    for (int m = 0; m < kSlotsA; ++m) {
+      if constexpr (kM) {
+        if ((m & 1) == 0 && m / 2 + kLookRA < 2 * kSd) rd(m / 2 + kLookRA);
+        __builtin_amdgcn_sched_barrier(0);
+        const int kk = m >> 2, qb = m & 1;
+        const u32x4 op = opa[(m >> 1) % (kLookRA + 1)];
+        if (m & 2) {
+          if (kk == 0) cur.dp[qb] = mfma32_va0<FP16>(op, oreg[qb][0]);
+          else mfma32_va<FP16>(op, oreg[qb][kk], cur.dp[qb]);
+        } else {
+          if (kk == 0) cur.s[qb] = mfma32_va0<FP16>(op, qreg[qb][0]);
+          else mfma32_va<FP16>(op, qreg[qb][kk], cur.s[qb]);
         }
-      u32x4 dsb[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) dsb[t] = pack_b<FP16>(s, t);
-      // dQ^T += K^T dS^T
-#pragma unroll
-      for (int st = 0; st < D / 8; ++st) {
-        const int t = st / (D / 32), db = st % (D / 32);
-        const u32x2 lo = lds_read_tr16(kt + t_off[0][db] + 16 * t * T::rowBytes);
-        const u32x2 hi = lds_read_tr16(kt + t_off[1][db] + 16 * t * T::rowBytes);
-        dq[db] = mfma32<FP16>(u32x4{lo[0], lo[1], hi[0], hi[1]}, dsb[t], dq[db]);
       }
+      if constexpr (kV) {
+#pragma unroll
+        for (int i = 0; i < kDqItems; ++i)
+          if (kM ? item_slot(i, kSlotsA, 2) == m : m == 0) item(mask, prev, 1, i, lim);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (i + 1 < n_tiles) {
-      if (i + kAhead < n_tiles) wait_vmcnt<kLoads>();
-      else wait_vmcnt<0>();
-      __syncthreads();
-    }
-  }
+  };
 
-  if (row_ok) store_rows<FP16, D>(reinterpret_cast<uint16_t*>(a.dq) + head + (int64_t)qrow * D, dq, a.scale, h);
+  // Phase B(j): dQ^T of sub-tile j - 1 from prev (MFMA) | items of block 0 of
+  // sub-tile j in cur (VALU) | the loads of sub-tile j + 2. Product m: operand pair
+  // m / 2 (k-step t, d block db) read through the transposing read, serving
+  // block m % 2.
+  constexpr int kLookRB = 2;  // transposing read pairs issued this many pairs ahead
+  auto phase_b = [&](auto mfma, auto valu, auto mask, int j, DqSub& cur, DqSub& prev, bool loads) {
+    constexpr bool kM = decltype(mfma)::value, kV = decltype(valu)::value;
+    const char* kp = stage(j - 1);
+    u32x2 lo[kLookRB + 1], hi[kLookRB + 1];
+    auto rd = [&](int s) {
+      const int t = s / (D / 32), db = s % (D / 32), sl = s % (kLookRB + 1);
+      lo[sl] = lds_read_tr16(kp + t_off[0][db] + 16 * t * T::rowBytes);
+      hi[sl] = lds_read_tr16(kp + t_off[1][db] + 16 * t * T::rowBytes);
+    };
+    if constexpr (kM) {
+#pragma unroll
+      for (int s = 0; s < kLookRB; ++s) rd(s);
+    }
+    const int lim = (kV ? lim0 : 0) - j * kSub - 4 * h;
+    const SubSrc ss = sub_src(j + 2);
+#pragma unroll
+    for (int m = 0; m < kSlotsB; ++m) {
+      if constexpr (kM) {
+        if ((m & 1) == 0 && m / 2 + kLookRB < kSlotsB / 2) rd(m / 2 + kLookRB);
+        __builtin_amdgcn_sched_barrier(0);
+        const int s = m >> 1, t = s / (D / 32), db = s % (D / 32), sl = s % (kLookRB + 1), qb = m & 1;
+        mfma32_aa<FP16>(u32x4{lo[sl][0], lo[sl][1], hi[sl][0], hi[sl][1]}, prev.dsb[qb][t], dq[qb][db]);
+      }
+      if (loads && m < kLoads) issue_load(ss, m);
+      if constexpr (kV) {
+#pragma unroll
+        for (int i = 0; i < kDqItems; ++i)
+          if (kM ? item_slot(i, kSlotsB, 4) == m : m == 0) item(mask, cur, 0, i, lim);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  using Y_ = std::true_type;
+  using N_ = std::false_type;
+  auto sub_end = [&]() {
+    wait_vmcnt<kLoads>();
+    __syncthreads();
+  };
+  auto trip = [&](auto mask, int j, DqSub& cur, DqSub& prev) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) asm volatile("" : "+a"(dq[qb][db]));
+    phase_a(Y_{}, Y_{}, mask, j, cur, prev);
+    phase_b(Y_{}, Y_{}, mask, j, cur, prev, true);
+    sub_end();
+  };
+  // the last sub-tile (in x): its block-1 items, then its dQ^T products
+  auto finish = [&](int j, DqSub& x) {
+    wait_vmcnt<0>();  // no load may still be writing LDS when the workgroup ends
+    mfma_wait(x.s[1], x.dp[1]);
+    phase_a(N_{}, Y_{}, Y_{}, j + 1, x, x);
+    phase_b(Y_{}, N_{}, Y_{}, j + 1, x, x, false);
+  };
+
+  DqSub X, Y;
+  // sub-tile 0: its products, then its block-0 items with nothing to overlap
+  phase_a(Y_{}, N_{}, N_{}, 0, X, Y);
+  mfma_wait(X.s[0], X.dp[0]);
+  phase_b(N_{}, Y_{}, Y_{}, 0, X, Y, true);
+  sub_end();
+  // Trips in pairs (sub-tiles j in Y, j + 1 in X), at least one pair, so that the
+  // last sub-tile is always in X; sub-tiles past the end are masked. A pair whose
+  // items (sub-tiles 2 p .. 2 p + 2) all precede m0 needs no mask.
+  const int pairs = max(1, n_sub >> 1);
+  const int p_u = min(pairs, max(0, (m0 - 1) / 2));
+  int p = 0;
+  for (; p < p_u; ++p) {
+    trip(N_{}, 2 * p + 1, Y, X);
+    trip(N_{}, 2 * p + 2, X, Y);
+  }
+  for (; p < pairs; ++p) {
+    trip(Y_{}, 2 * p + 1, Y, X);
+    trip(Y_{}, 2 * p + 2, X, Y);
+  }
+  finish(2 * pairs, X);
+
+  mfma_drain_a<D / 32>(dq[0], dq[1]);
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+    if (qrow[qb] < N)
+      store_rows<FP16, D>(reinterpret_cast<uint16_t*>(a.dq) + head + (int64_t)qrow[qb] * D, dq[qb], a.scale, h);
 }
 
 // ------------------------------------------------------------------------------

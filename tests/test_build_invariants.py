@@ -1,8 +1,9 @@
 """Properties of the generated gfx950 code that the kernels' correctness relies on.
 
-The dK/dV kernel of the backward pass issues its matrix products as inline
-assembly with fixed register classes (K, V, dK, dV in accumulation registers, S
-and dP in vector registers) and inserts the wait states around them itself,
+The dK/dV and dQ kernels of the backward pass issue their matrix products as
+inline assembly with fixed register classes (K, V, dK, dV, or Q, dO, dQ in
+accumulation registers; S and dP in vector registers) and insert the wait states
+around them themselves,
 because the compiler's hazard checks do not see an MFMA inside an asm statement.
 That is sound only while the compiler neither spills nor moves those registers
 inside the tile loop: a copy or spill placed right after such a product would
@@ -63,10 +64,10 @@ def _blocks(asm: str, kernel: str):
 
 @pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
                     reason="hipcc not available")
-def test_dkdv_product_blocks_have_no_moves_or_spills():
+def test_backward_product_blocks_have_no_moves_or_spills():
     asm = _assembly(os.path.join(ROOT, "exact_attention_flash_amd", "csrc", "bwd_kernel.hip"))
-    kernels = re.findall(r"^(_ZN2fa3bwd8bwd_dkdv\S+):", asm, re.M)
-    assert len(kernels) == 8  # {bf16, fp16} x {64, 128} x {causal, not}
+    kernels = re.findall(r"^(_ZN2fa3bwd(?:8bwd_dkdv|6bwd_dq)\S+):", asm, re.M)
+    assert len(kernels) == 16  # {dK/dV, dQ} x {bf16, fp16} x {64, 128} x {causal, not}
     for k in kernels:
         for name, ins in _blocks(asm, k):
             at = [n for n, i in enumerate(ins) if "mfma" in i]
