@@ -300,7 +300,7 @@ def run_bwd(args, workload_name, causal):
                    "dtype": w.dtype, "pass": "backward"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "kernel": "bwd_delta + bwd_dq + bwd_dkdv (flash_attn_bwd)", "flop_per_launch": flops,
+                     "kernel": "bwd_dq + bwd_dkdv (flash_attn_bwd)", "flop_per_launch": flops,
                      "launch_ms": round(g["event_ms_per_launch"], 5),
                      "launch_ms_median": round(g["launch_ms_median"], 5)},
         "extra_alloc_bytes": g["extra_alloc_bytes"], "device": g["device"],

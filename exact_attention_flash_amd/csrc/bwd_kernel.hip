@@ -7,17 +7,18 @@
 // P = exp(S - L) from Q, K and L and forms
 //     dV = P^T dO,  dP = dO V^T,  dS = P ∘ (dP - D),  dQ = scale dS K,  dK = scale dS^T Q,
 // with D_i = rowsum(dO ∘ O)_i (the identity rowsum(dP ∘ P) = rowsum(dO ∘ O) of
-// V1 §6.1). Three kernels run in order on one stream:
-//  1. bwd_delta: D = rowsum(dO ∘ O) in fp32, one value per query row.
-//  2. bwd_dq: a workgroup owns 256 query rows (4 waves of 64, one wave per SIMD)
+// V1 §6.1). Two kernels run in order on one stream:
+//  1. bwd_dq: a workgroup owns 256 query rows (4 waves of 64, one wave per SIMD)
 //     and streams key sub-tiles of 32 rows through LDS. Per sub-tile each wave
 //     forms S^T = K Q^T and dP^T = V dO^T for its two 32-row query blocks (MFMA,
 //     operands K and V rows from LDS, each read serving both blocks; Q and dO
 //     rows in registers), P^T = exp2(S^T scale log2 e - L log2 e),
 //     dS^T = P^T ∘ (dP^T - D), and accumulates dQ^T += K^T dS^T with K^T read
 //     through the transposing LDS read and dS^T rounded to 16 bits as the B
-//     operand without leaving registers; software-pipelined like bwd_dkdv.
-//  3. bwd_dkdv: a workgroup owns 128 keys (4 waves of 32, one wave per SIMD, so
+//     operand without leaving registers; software-pipelined like bwd_dkdv. It
+//     first forms D for its rows in fp32 (from the dO rows it holds and the O
+//     rows it loads) and stores it for bwd_dkdv.
+//  2. bwd_dkdv: a workgroup owns 128 keys (4 waves of 32, one wave per SIMD, so
 //     each wave has the whole register file) and streams query tiles of 64 rows
 //     (Q, dO, L and D) through LDS. Per tile each wave forms S = Q K^T and
 //     dP = dO V^T (K and V rows of its keys in registers), P and dS as above,
@@ -164,42 +165,7 @@ __device__ __forceinline__ void store_rows(uint16_t* row_ptr, const f32x16 (&acc
 }
 
 // ------------------------------------------------------------------------------
-// 1. D = rowsum(dO ∘ O): 16-byte chunks, D/8 lanes per row, fp32 products and sums.
-template <bool FP16, int D>
-__global__ __launch_bounds__(256) void bwd_delta(BwdArgs a) {
-  constexpr int kLanesPerRow = D / 8;
-  constexpr int kRowsPerBlock = 256 / kLanesPerRow;
-  const int64_t rows = (int64_t)a.bh * a.n;
-  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kLanesPerRow;
-  const int part = threadIdx.x % kLanesPerRow;
-  float acc = 0.f;
-  if (row < rows) {
-    const u32x4 x = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.dout) + row * D + part * 8);
-    const u32x4 y = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.o) + row * D + part * 8);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float x0, x1, y0, y1;
-      if constexpr (FP16) {
-        // element copies first: a bit cast applied to a vector element expression
-        // directly has been compiled as a cast of element 0
-        const uint32_t xi = x[i], yi = y[i];
-        const f16x2 xv = __builtin_bit_cast(f16x2, xi), yv = __builtin_bit_cast(f16x2, yi);
-        x0 = (float)xv[0]; x1 = (float)xv[1]; y0 = (float)yv[0]; y1 = (float)yv[1];
-      } else {
-        x0 = __uint_as_float(x[i] << 16); x1 = __uint_as_float(x[i] & 0xffff0000u);
-        y0 = __uint_as_float(y[i] << 16); y1 = __uint_as_float(y[i] & 0xffff0000u);
-      }
-      acc = __builtin_fmaf(x0, y0, acc);
-      acc = __builtin_fmaf(x1, y1, acc);
-    }
-  }
-#pragma unroll
-  for (int m = 1; m < kLanesPerRow; m <<= 1) acc += __shfl_xor(acc, m, kLanesPerRow);
-  if (row < rows && part == 0) a.delta[row] = acc;
-}
-
-// ------------------------------------------------------------------------------
-// 2. dQ: 4 waves x 64 query rows (one wave per SIMD), key sub-tiles of 32 streamed
+// 1. dQ (and D): 4 waves x 64 query rows (one wave per SIMD), key sub-tiles of 32 streamed
 // through LDS.
 //
 // Each wave owns two 32-row query blocks, so every K, V or K^T operand it reads
@@ -223,6 +189,31 @@ struct DqSub {
   f32x16 s[2], dp[2];
   u32x4 dsb[2][2];
 };
+
+// One 16-bit value of a 32-bit word (half 0: low bits) widened to fp32.
+template <bool FP16>
+__device__ __forceinline__ float widen16(uint32_t w, int half) {
+  const uint32_t bits = half ? (w >> 16) : (w & 0xffffu);
+  if constexpr (FP16) return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+  else return __uint_as_float(bits << 16);
+}
+
+// Sum of the 8 products of two 16-byte vectors of 16-bit values, in fp32, each
+// value widened from its 32-bit word with integer operations. (Widening an element
+// of the vector through a bit cast to a two-element fp16 vector made the compiler
+// read element 0 for every element, fused into v_dot2c_f32_f16 or not: the sum held
+// one quarter of the products four times.)
+template <bool FP16>
+__device__ __forceinline__ float dot8(u32x4 x, u32x4 y) {
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t xw = x[i], yw = y[i];
+    acc = __builtin_fmaf(widen16<FP16>(xw, 0), widen16<FP16>(yw, 0), acc);
+    acc = __builtin_fmaf(widen16<FP16>(xw, 1), widen16<FP16>(yw, 1), acc);
+  }
+  return acc;
+}
 
 template <bool FP16>
 __device__ __forceinline__ u32x4 pack_b1(const f32x16& v, int t) {
@@ -311,23 +302,42 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void bwd_dq(BwdArgs a) {
   issue_sub(0);
   issue_sub(1);
   // Q and dO rows of this lane's queries (B operands, k-slots d = 16 kk + 8 h + 0..7),
-  // L log2 e and D of the queries (rows past N read as zeros and are never stored)
+  // L log2 e of the queries, and D = rowsum(dO ∘ O): each lane of a query holds half
+  // its dO row and loads the same half of its O row, and the two halves meet with one
+  // lane swap. D is stored for the dK/dV kernel (rows past N read as zeros and are
+  // never stored).
   u32x4 qreg[2][kSd], oreg[2][kSd];
   float lse2[2], dlt[2];
   {
     const __amdgpu_buffer_rsrc_t qr = buffer_rsrc(reinterpret_cast<const uint16_t*>(a.q) + head, head_bytes);
     const __amdgpu_buffer_rsrc_t dr = buffer_rsrc(reinterpret_cast<const uint16_t*>(a.dout) + head, head_bytes);
+    const __amdgpu_buffer_rsrc_t orr = buffer_rsrc(reinterpret_cast<const uint16_t*>(a.o) + head, head_bytes);
+    u32x4 orow[2][kSd];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
       for (int kk = 0; kk < kSd; ++kk) {
         qreg[qb][kk] = buffer_load16(qr, (uint32_t)qrow[qb] * T::rowBytes + kk * 32 + h * 16);
         oreg[qb][kk] = buffer_load16(dr, (uint32_t)qrow[qb] * T::rowBytes + kk * 32 + h * 16);
+        orow[qb][kk] = buffer_load16(orr, (uint32_t)qrow[qb] * T::rowBytes + kk * 32 + h * 16);
       }
       const bool ok = qrow[qb] < N;
       lse2[qb] = ok ? a.lse[(int64_t)bh * N + qrow[qb]] * kLog2e : 0.f;
-      dlt[qb] = ok ? a.delta[(int64_t)bh * N + qrow[qb]] : 0.f;
     }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float part = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < kSd; ++kk) part += dot8<FP16>(oreg[qb][kk], orow[qb][kk]);
+      dlt[qb] = part + other_half(part);
+      if (h == 0 && qrow[qb] < N) a.delta[(int64_t)bh * N + qrow[qb]] = dlt[qb];
+    }
+    // the B operands move into the accumulation registers here, before the first
+    // product reads them (the statement fixes where the copies happen)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int kk = 0; kk < kSd; ++kk) asm volatile("" : "+a"(qreg[qb][kk]), "+a"(oreg[qb][kk]));
   }
   const float c = a.scale_log2;
   wait_vmcnt<0>();
@@ -513,7 +523,7 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void bwd_dq(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------------------
-// 3. dK, dV: 4 waves x 32 keys, query tiles of 64 (Q, dO, L, D) streamed through LDS.
+// 2. dK, dV: 4 waves x 32 keys, query tiles of 64 (Q, dO, L, D) streamed through LDS.
 //
 // One wave per SIMD, so nothing but the wave's own instruction order overlaps its
 // matrix work with its VALU work. The loop is software-pipelined over tiles: the
@@ -846,20 +856,15 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv(BwdArgs a) {
 
 template <bool FP16, int D, bool CAUSAL>
 hipError_t launch_all(const BwdArgs& a, hipStream_t stream) {
-  const int64_t rows = (int64_t)a.bh * a.n;
-  constexpr int kRowsPerBlock = 256 / (D / 8);
-  hipLaunchKernelGGL((bwd_delta<FP16, D>), dim3((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)), dim3(256), 0,
-                     stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  // D = rowsum(dO ∘ O) is formed by bwd_dq (each workgroup for its own rows) and
+  // stored for bwd_dkdv, which runs after it on the same stream
   const int q_tiles = (a.n + kDqRows - 1) / kDqRows;
   const int k_blocks = (a.n + kKvRows - 1) / kKvRows;
-  launch_log("bwd_delta<%s, %d> grid %lld x 256; bwd_dq<%s, %d, %s> grid %d x %d; bwd_dkdv<%s, %d, %s> grid %d x %d",
-             dtype_name(FP16), D, (long long)((rows + kRowsPerBlock - 1) / kRowsPerBlock), dtype_name(FP16), D,
+  launch_log("bwd_dq<%s, %d, %s> grid %d x %d; bwd_dkdv<%s, %d, %s> grid %d x %d", dtype_name(FP16), D,
              CAUSAL ? "causal" : "full", a.bh * q_tiles, 64 * kDqWaves, dtype_name(FP16), D,
              CAUSAL ? "causal" : "full", a.bh * k_blocks, 64 * kKvWaves);
   hipLaunchKernelGGL((bwd_dq<FP16, D, CAUSAL>), dim3(a.bh * q_tiles), dim3(64 * kDqWaves), 0, stream, a);
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_dkdv<FP16, D, CAUSAL>), dim3(a.bh * k_blocks), dim3(64 * kKvWaves), 0, stream, a);
   return hipGetLastError();

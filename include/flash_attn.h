@@ -364,7 +364,7 @@ int flash_attn_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, 
  *           B * H * ceil(N / 128) < 2^31.
  *
  * Ownership, streams and errors as for flash_attn_fwd: nothing is allocated,
- * three kernels are enqueued on `stream` and nothing is synchronised. Alignment:
+ * two kernels are enqueued on `stream` and nothing is synchronised. Alignment:
  * the 16-bit tensors 16-byte aligned, lse and delta 4-byte aligned
  * (FA_ERR_ALIGN). dq, dk, dv and delta must not overlap each other or any input
  * (FA_ERR_ALIAS).

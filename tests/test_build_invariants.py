@@ -280,3 +280,16 @@ def test_inline_asm_wait_states(source):
         lds_loads += sum(1 for blk in _function(asm, k)[0] for i in blk if i.startswith("buffer_load") and i.endswith("lds"))
     assert lds_loads > 0
     assert not bad, "\n".join(bad[:20]) + f"\n({len(bad)} in all)"
+
+
+@pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
+                    reason="hipcc not available")
+@pytest.mark.parametrize("source", ["fwd_kernel.hip", "fwd_sp.hip", "bwd_kernel.hip", "fwd_fp8.hip"])
+def test_no_fused_dot2(source):
+    """No kernel may contain v_dot2*: the compiler once fused the fp16 widening and
+    FMAs of the dQ kernel's D = rowsum(dO ∘ O) into v_dot2c_f32_f16 and issued the
+    first pair's operands for all four pairs of a 16-byte vector, so D held a quarter
+    of the sum four times. The kernels keep such sums as widened FMAs."""
+    asm = _assembly(os.path.join(ROOT, "exact_attention_flash_amd", "csrc", source))
+    dots = sorted({ln.split()[0] for ln in asm.split("\n") if ln.strip().startswith("v_dot2")})
+    assert not dots, f"{source}: {dots}"
