@@ -38,6 +38,7 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "bwd_kernel.h"
 #include "gfx950_ops.h"
@@ -162,6 +163,25 @@ __device__ __forceinline__ void store_rows(uint16_t* row_ptr, const f32x16 (&acc
                        pack2<FP16>(acc[db][4 * g + 2] * mul, acc[db][4 * g + 3] * mul)};
       *reinterpret_cast<u32x2*>(row_ptr + db * 32 + 8 * g + 4 * h) = w;
     }
+}
+
+// x of lane N of the lane's 16-lane row (DPP row_newbcast:N), for the VALU
+// instruction that consumes it: the compiler folds the move into a two-operand
+// subtraction (v_subrev_f32_dpp)
+template <int N>
+__device__ __forceinline__ float row_bcast(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + N, 0xf, 0xf, true));
+}
+
+// f(std::integral_constant<int, i>) for i = 0 .. N - 1 in order: code generated per i,
+// with i a constant expression (no loop for the compiler to unroll)
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // ------------------------------------------------------------------------------
@@ -652,6 +672,7 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv(BwdArgs a) {
     }
   }
   const float c = a.scale_log2;
+  const float inv_scale = 1.f / a.scale;
   wait_vmcnt<0>();
   __syncthreads();
 
@@ -682,33 +703,40 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv(BwdArgs a) {
   // precedes the key (MASK), and dS = P (dP - D) in place; items 8, 9 (18, 19) pack
   // P and dS of elements 0-7 (8-15) into the B operand of k-step 2 b (2 b + 1).
   // lim = key - (first query row of the tile) - 4 h: element 4 g + r is masked when
-  // 32 b + 8 g + r < lim.
-  auto item = [&](auto mask, KvTile& x, int b, int i, const f32x4 (&l4)[4], const f32x4 (&d4)[4], int lim) {
-    if (i == 8 || i == 18) {
+  // 32 b + 8 g + r < lim. A row's L / scale and D come from the block's compact
+  // registers cl, cd (lane k of each 16-lane row holds row 16 q + k + 4 h of the
+  // block, q = g / 2) by a broadcast of lane 8 (g % 2) + r into the subtraction
+  // (S - L / scale) scale log2 e, whose operands no VALU instruction has just written.
+  auto item = [&](auto mask, KvTile& x, int b, auto ic, const float (&cl)[2], const float (&cd)[2], int lim) {
+    constexpr int i = decltype(ic)::value;
+    if constexpr (i == 8 || i == 18) {
       x.pb[2 * b + i / 18] = pack_b<FP16>(x.s, 2 * b + i / 18);
-    } else if (i == 9 || i == 19) {
+    } else if constexpr (i == 9 || i == 19) {
       x.dsb[2 * b + i / 19] = pack_b<FP16>(x.dp, 2 * b + i / 19);
     } else {
-      const int e = i < 8 ? i : i - 2, g = e >> 2, r = e & 3;
-      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(x.s[b][e], c, -l4[g][r] * kLog2e));
+      constexpr int e = i < 8 ? i : i - 2, g = e >> 2, r = e & 3, n = 8 * (g & 1) + r;
+      float p = __builtin_amdgcn_exp2f((x.s[b][e] - row_bcast<n>(cl[g >> 1])) * c);
       if constexpr (decltype(mask)::value) p = (32 * b + 8 * g + r < lim) ? 0.f : p;
       x.s[b][e] = p;
-      x.dp[b][e] = p * (x.dp[b][e] - d4[g][r]);
+      x.dp[b][e] = p * (x.dp[b][e] - row_bcast<n>(cd[g >> 1]));
     }
   };
   // slot (product index within a phase) after which item i runs: the items start a
   // few products into the phase (their L and D reads are then in) and spread evenly
-  auto item_slot = [](int i) {
+  auto item_slot = [](int i) constexpr {
     constexpr int first = kSlots >= 32 ? 2 : 1;
     return first + (i * (kSlots - first)) / kItems;
   };
-  auto read_stats = [&](const char* st, int b, f32x4 (&l4)[4], f32x4 (&d4)[4]) {
+  // the block's compact L / scale and D registers (see item); the row index is
+  // clamped to the tile (the lanes past row 63 feed no element)
+  auto read_stats = [&](const char* st, int b, float (&cl)[2], float (&cd)[2]) {
     const float* lt = reinterpret_cast<const float*>(st + 2 * T::bytes);
     const float* dt = reinterpret_cast<const float*>(st + 2 * T::bytes + kStat);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      l4[g] = *reinterpret_cast<const f32x4*>(lt + 32 * b + 8 * g + 4 * h);
-      d4[g] = *reinterpret_cast<const f32x4*>(dt + 32 * b + 8 * g + 4 * h);
+    for (int q = 0; q < 2; ++q) {
+      const int row = min(32 * b + 16 * q + (lane & 15) + 4 * h, kTile - 1);
+      cl[q] = lt[row] * inv_scale;
+      cd[q] = dt[row];
     }
   };
 
@@ -727,34 +755,34 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv(BwdArgs a) {
 #pragma unroll
       for (int m = 0; m < kLookA; ++m) rd(m);
     }
-    f32x4 l4[4], d4[4];
+    float l4[2], d4[2];
     int lim = 0;
     if constexpr (kV) {
       read_stats(stage(j - 1), 1, l4, d4);
       lim = key - (t_first + j - 1) * kTile - 4 * h;
     }
-#pragma unroll
-    for (int m = 0; m < kSlots; ++m) {
+    static_for<kSlots>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
       if constexpr (kM) {
-        if (m + kLookA < kSlots) rd(m + kLookA);
+        if constexpr (m + kLookA < kSlots) rd(m + kLookA);
         __builtin_amdgcn_sched_barrier(0);
-        const int b = m / (2 * kSd), kk = (m >> 1) % kSd;
+        constexpr int b = m / (2 * kSd), kk = (m >> 1) % kSd;
         const u32x4 op = opa[m % (kLookA + 1)];
-        if (m & 1) {
-          if (kk == 0) cur.dp[b] = mfma32_va0<FP16>(op, vreg[0]);
+        if constexpr (m & 1) {
+          if constexpr (kk == 0) cur.dp[b] = mfma32_va0<FP16>(op, vreg[0]);
           else mfma32_va<FP16>(op, vreg[kk], cur.dp[b]);
         } else {
-          if (kk == 0) cur.s[b] = mfma32_va0<FP16>(op, kreg[0]);
+          if constexpr (kk == 0) cur.s[b] = mfma32_va0<FP16>(op, kreg[0]);
           else mfma32_va<FP16>(op, kreg[kk], cur.s[b]);
         }
       }
       if constexpr (kV) {
-#pragma unroll
-        for (int i = 0; i < kItems; ++i)
-          if (kM ? item_slot(i) == m : m == 0) item(mask, prev, 1, i, l4, d4, lim);
+        static_for<kItems>([&](auto ic) {
+          if constexpr (kM ? item_slot(decltype(ic)::value) == m : m == 0) item(mask, prev, 1, ic, l4, d4, lim);
+        });
       }
       __builtin_amdgcn_sched_barrier(0);
-    }
+    });
   };
 
   // Phase B(j): dV and dK of tile j - 1 from prev (MFMA) | items of query block 0
@@ -774,31 +802,33 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv(BwdArgs a) {
 #pragma unroll
       for (int m = 0; m < kLookB; ++m) rd(m);
     }
-    f32x4 l4[4], d4[4];
+    float l4[2], d4[2];
     int lim = 0;
     if constexpr (kV) {
       read_stats(stage(j), 0, l4, d4);
       lim = key - (t_first + j) * kTile - 4 * h;
     }
     const TileSrc ts = tile_src(j + 2);
-#pragma unroll
-    for (int m = 0; m < kSlots; ++m) {
+    static_for<kSlots>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
       if constexpr (kM) {
-        if (m + kLookB < kSlots) rd(m + kLookB);
+        if constexpr (m + kLookB < kSlots) rd(m + kLookB);
         __builtin_amdgcn_sched_barrier(0);
-        const int s = m >> 1, t = s / (D / 32), db = s % (D / 32), sl = m % (kLookB + 1);
+        constexpr int s = m >> 1, t = s / (D / 32), db = s % (D / 32), sl = m % (kLookB + 1);
         const u32x4 opnd = u32x4{lo[sl][0], lo[sl][1], hi[sl][0], hi[sl][1]};
-        if (m & 1) mfma32_aa<FP16>(opnd, prev.dsb[t], dk[db]);
+        if constexpr (m & 1) mfma32_aa<FP16>(opnd, prev.dsb[t], dk[db]);
         else mfma32_aa<FP16>(opnd, prev.pb[t], dv[db]);
       }
-      if (loads && m < kLoads) issue_load(ts, m);
+      if constexpr (m < kLoads) {
+        if (loads) issue_load(ts, m);
+      }
       if constexpr (kV) {
-#pragma unroll
-        for (int i = 0; i < kItems; ++i)
-          if (kM ? item_slot(i) == m : m == 0) item(mask, cur, 0, i, l4, d4, lim);
+        static_for<kItems>([&](auto ic) {
+          if constexpr (kM ? item_slot(decltype(ic)::value) == m : m == 0) item(mask, cur, 0, ic, l4, d4, lim);
+        });
       }
       __builtin_amdgcn_sched_barrier(0);
-    }
+    });
   };
 
   using Y_ = std::true_type;
